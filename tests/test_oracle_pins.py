@@ -1,0 +1,392 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a library routine
+(scipy softmax, numpy argmax), a closed form, an invariant the pages state, a case whose
+answer follows by hand from the definition, the pages' worked example, or the distribution
+of the output (chi-square, and exact stratified grids).  Between them a dropped term, a
+wrong sign, a swapped operand (p/q vs q/p, (p-q)+ vs (q-p)+), a wrong row or uniform
+index, a wrong temperature placement or a non-strict comparison fails at least one test.
+"""
+import json
+from pathlib import Path
+
+import numpy as np
+import pytest
+from scipy import special
+
+import oracle
+import workloads
+from workloads import Workload
+from tests.stats_util import chi2_pvalue
+
+GOLDEN = Path(__file__).resolve().parent / "golden"
+
+
+def _softmax(z, T):
+    return special.softmax(np.asarray(z, dtype=np.float64) / T)
+
+
+def _explicit(target, draft, tokens, uniforms, T, gamma, dtype="f32", cu=None):
+    """Workload from explicit float64 rows (encoded to ``dtype``)."""
+    target = workloads.encode(np.asarray(target, dtype=np.float64), dtype)
+    draft = workloads.encode(np.asarray(draft, dtype=np.float64).reshape(-1, target.shape[1]),
+                             dtype)
+    uniforms = np.asarray(uniforms, dtype=np.float32).reshape(-1, 2)
+    B = target.shape[0] - draft.shape[0]
+    temps = np.broadcast_to(np.asarray(T, dtype=np.float32), (B,)).copy()
+    return Workload("explicit", dtype, B, gamma, target.shape[1], target, draft,
+                    np.asarray(tokens, dtype=np.int32), uniforms, temps,
+                    None if cu is None else np.asarray(cu, dtype=np.int32))
+
+
+# --------------------------------------------------------------------------- library routines
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [0.05, 0.7, 1.0, 3.0])
+def test_row_statistics_and_probabilities_match_scipy_softmax(dtype, T):
+    w = workloads.small(B=5, gamma=3, V=257, dtype=dtype, seed=11, temperatures=T)
+    r = oracle.verify(w)
+    T = float(np.float32(T))    # temperatures are passed as float32
+    zt = workloads.decode(w.target, dtype)
+    zd = workloads.decode(w.draft, dtype)
+    for row in range(w.R_t):
+        m = zt[row].max()
+        assert r["row_max_t"][row] == m
+        S_ref = np.exp(special.logsumexp((zt[row] - m) / T))
+        assert r["row_sum_t"][row] == pytest.approx(S_ref, rel=1e-12)
+    for row in range(w.R_d):
+        assert r["row_max_d"][row] == zd[row].max()
+    tb, db = w.target_base, w.draft_base
+    for b in range(w.B):
+        for i in range(w.gamma):
+            x = w.draft_tokens[db[b] + i]
+            p_ref = _softmax(zt[tb[b] + i], T)[x]
+            q_ref = _softmax(zd[db[b] + i], T)[x]
+            assert r["p_x"][db[b] + i] == pytest.approx(p_ref, rel=1e-12, abs=1e-300)
+            assert r["q_x"][db[b] + i] == pytest.approx(q_ref, rel=1e-12, abs=1e-300)
+
+
+def _argmax_decoding(w):
+    """Greedy verification written as target-argmax decoding with numpy.argmax
+    (first occurrence of the maximum)."""
+    zt = workloads.decode(w.target, w.dtype)
+    out = np.full(w.R_t, -1, dtype=np.int32)
+    nacc = np.zeros(w.B, dtype=np.int32)
+    for b, (tb, db, g) in enumerate(zip(w.target_base, w.draft_base, w.gammas)):
+        am = [int(np.argmax(zt[tb + i])) for i in range(g + 1)]
+        n = g
+        for i in range(g):
+            if w.draft_tokens[db + i] != am[i]:
+                n = i
+                break
+        out[tb: tb + n] = w.draft_tokens[db: db + n]
+        out[tb + n] = am[n]
+        nacc[b] = n
+    return out, nacc
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("ragged", [False, True])
+def test_greedy_equals_target_argmax_decoding(dtype, ragged):
+    # Speculative Decoding : accélérer l'inférence des LLM, 'Pourquoi la qualité est
+    # préservée' (temperature zero); Speculative Decoding wiki, '実装上の注意'.
+    w = workloads.small(B=300, gamma=5, V=50, dtype=dtype, seed=3, temperatures=0.0,
+                        draft_sigma=0.5, ragged=ragged)
+    ref_out, ref_n = _argmax_decoding(w)
+    for greedy_flag in (False, True):
+        r = oracle.verify(w, greedy=greedy_flag)
+        np.testing.assert_array_equal(r["out_tokens"], ref_out)
+        np.testing.assert_array_equal(r["num_accepted"], ref_n)
+    # the mix must contain both full acceptance and early rejection
+    assert (ref_n == w.gammas).any() and (ref_n < w.gammas).any()
+
+
+def test_greedy_ties_resolve_to_lowest_index():
+    V = 12
+    t = np.full((3, V), -1.0)
+    t[0, [7, 3]] = 2.5          # tie at the maximum: argmax is 3
+    t[1, :] = -2.0
+    t[1, 9] = 0.0               # +0.0 and -0.0 tie at the maximum: argmax is 5
+    t[1, 5] = -0.0
+    t[2, [0, 11]] = 4.0         # bonus row: argmax 0
+    for dtype in ("f32", "bf16"):
+        # draft 3 (lowest tied index) accepted, then draft 9 rejected in favour of 5
+        w = _explicit(t, np.zeros((2, V)), [3, 9], np.zeros((3, 2)), 0.0, 2, dtype)
+        r = oracle.verify(w)
+        assert list(r["out_tokens"]) == [3, 5, -1] and r["num_accepted"][0] == 1
+        # draft 7 is a maximum too, but not the lowest-index one: rejected, 3 emitted
+        w = _explicit(t, np.zeros((2, V)), [7, 5], np.zeros((3, 2)), 0.0, 2, dtype)
+        r = oracle.verify(w)
+        assert list(r["out_tokens"]) == [3, -1, -1] and r["num_accepted"][0] == 0
+        # both accepted: bonus is the bonus row's lowest-index argmax
+        w = _explicit(t, np.zeros((2, V)), [3, 5], np.zeros((3, 2)), 0.0, 2, dtype)
+        r = oracle.verify(w)
+        assert list(r["out_tokens"]) == [3, 5, 0] and r["num_accepted"][0] == 2
+
+
+# --------------------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_p_equal_q_accepts_every_draft(dtype):
+    # min(1, p/q) = 1 when p = q, and u < 1 always.
+    w = workloads.small(B=64, gamma=6, V=300, dtype=dtype, seed=5, temperatures=0.8,
+                        ragged=True)
+    for b, (tb, db, g) in enumerate(zip(w.target_base, w.draft_base, w.gammas)):
+        w.draft[db: db + g] = w.target[tb: tb + g]
+    # draft tokens drawn from the new q (= p)
+    rng = np.random.default_rng(99)
+    w.draft_tokens[:] = workloads.draw_draft_tokens(workloads.decode(w.draft, dtype), 0.8, rng)
+    w.uniforms[:, 0] = np.float32(np.nextafter(np.float32(1), np.float32(0)))  # worst case u
+    r = oracle.verify(w)
+    np.testing.assert_array_equal(r["num_accepted"], w.gammas)
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_emitted_count_prefix_and_residual_support(seed):
+    # Between 1 and gamma_b + 1 tokens per step; the accepted prefix is the drafts; the
+    # replacement is drawn where p > q, so never the rejected draft itself.
+    temps = np.where(np.arange(40) % 5 == 0, 0.0, np.linspace(0.3, 1.5, 40))
+    w = workloads.small(B=40, gamma=7, V=120, dtype="bf16", seed=seed, temperatures=temps,
+                        ragged=True, draft_sigma=1.0)
+    r = oracle.verify(w)
+    zt = workloads.decode(w.target, w.dtype)
+    zd = workloads.decode(w.draft, w.dtype)
+    for b, (tb, db, g) in enumerate(zip(w.target_base, w.draft_base, w.gammas)):
+        n = r["num_accepted"][b]
+        slots = r["out_tokens"][tb: tb + g + 1]
+        assert 0 <= n <= g
+        assert (slots[: n + 1] >= 0).all() and (slots[n + 1:] == -1).all()
+        np.testing.assert_array_equal(slots[:n], w.draft_tokens[db: db + n])
+        T = w.temperatures[b]
+        if T > 0 and n < g:
+            k = slots[n]
+            p = _softmax(zt[tb + n], T)
+            q = _softmax(zd[db + n], T)
+            assert p[k] > q[k]
+            assert k != w.draft_tokens[db + n]
+
+
+def test_ragged_layout_equals_requests_run_alone():
+    w = workloads.small(B=12, gamma=6, V=90, dtype="f32", seed=8, ragged=True,
+                        temperatures=np.linspace(0.0, 1.2, 12))
+    r = oracle.verify(w)
+    for b, (tb, db, g) in enumerate(zip(w.target_base, w.draft_base, w.gammas)):
+        one = Workload("one", w.dtype, 1, int(g), w.V, w.target[tb: tb + g + 1],
+                       w.draft[db: db + g], w.draft_tokens[db: db + g],
+                       w.uniforms[tb: tb + g + 1], w.temperatures[b: b + 1], None)
+        r1 = oracle.verify(one)
+        np.testing.assert_array_equal(r1["out_tokens"], r["out_tokens"][tb: tb + g + 1])
+        assert r1["num_accepted"][0] == r["num_accepted"][b]
+
+
+def test_request_subset_leaves_other_requests_untouched():
+    w = workloads.small(B=10, gamma=3, V=64, seed=4)
+    full = oracle.verify(w)
+    part = oracle.verify(w, requests=[2, 7])
+    for b in range(10):
+        tb = w.target_base[b]
+        if b in (2, 7):
+            np.testing.assert_array_equal(part["out_tokens"][tb: tb + 4],
+                                          full["out_tokens"][tb: tb + 4])
+        else:
+            assert (part["out_tokens"][tb: tb + 4] == -2).all()
+
+
+# --------------------------------------------------------------------------- cases by hand
+
+def test_residual_supported_on_one_token():
+    # target row 0: logits (0,0,0,3) -> p(3) ~ 0.864, the others ~ 0.045; draft row 0
+    # uniform (q = 1/4 each).  p - q > 0 only at token 3, so after any rejection the
+    # replacement is 3 whatever the uniform.  Draft x = 0: ratio p(0)/q(0) ~ 0.18.
+    t = [[0, 0, 0, 3], [5, 0, 0, 0]]
+    d = [[0, 0, 0, 0]]
+    for u_sample in (0.0, 0.3, 0.999):
+        w = _explicit(t, d, [0], [[0.5, u_sample], [0.0, 0.5]], 1.0, 1)
+        r = oracle.verify(w)
+        assert list(r["out_tokens"]) == [3, -1] and r["num_accepted"][0] == 0
+    # u = 0.1 < 0.18: accepted; the bonus comes from target row 1, where p(0) ~ 0.98, so a
+    # sample draw of 0.5 lands on token 0.
+    w = _explicit(t, d, [0], [[0.1, 0.99], [0.99, 0.5]], 1.0, 1)
+    r = oracle.verify(w)
+    assert list(r["out_tokens"]) == [0, 0] and r["num_accepted"][0] == 1
+
+
+def test_uniform_roles_and_strict_inverse_cdf():
+    # target row 0: logits (0,0,2,2); draft row 0 uniform.  p = (a,a,c,c) with a ~ 0.0596,
+    # c ~ 0.4404; q = 1/4.  (p-q)+ = (0,0,r,r): the residual puts exactly 1/2 on tokens 2 and
+    # 3.  Draft x = 0 has ratio a/(1/4) ~ 0.238.
+    t = [[0, 0, 2, 2], [0, 0, 2, 2]]
+    d = [[0, 0, 0, 0]]
+    # accept test uses u[0][0] = 0.9 -> reject (using u[0][1] = 0.2 would accept);
+    # the draw uses u[0][1] = 0.2 -> token 2 (using u[0][0] = 0.9 would give 3)
+    r = oracle.verify(_explicit(t, d, [0], [[0.9, 0.2], [0.0, 0.0]], 1.0, 1))
+    assert list(r["out_tokens"]) == [2, -1]
+    r = oracle.verify(_explicit(t, d, [0], [[0.9, 0.7], [0.0, 0.0]], 1.0, 1))
+    assert list(r["out_tokens"]) == [3, -1]
+    # u exactly at the CDF step (1/2): the strict C_k > u R picks the next token, 3
+    r = oracle.verify(_explicit(t, d, [0], [[0.9, 0.5], [0.0, 0.0]], 1.0, 1))
+    assert list(r["out_tokens"]) == [3, -1]
+    assert r["cdf_gap"][0] == 0.0
+    # accepted (0.1 < 0.238): the bonus draw is u[1][1] = 0.3 on p of row 1, whose CDF is
+    # (0.06, 0.12, 0.56, 1.0) -> token 2 (u[0][1] = 0.05 would give 0, u[1][0] = 0.99 would
+    # give 3)
+    r = oracle.verify(_explicit(t, d, [0], [[0.1, 0.05], [0.99, 0.3]], 1.0, 1))
+    assert list(r["out_tokens"]) == [0, 2]
+
+
+def test_temperature_divides_logits():
+    # p = softmax(z / T): with logits (0, ln 3) and T = 0.5 the target gives p = (1/10, 9/10)
+    # (softmax(z * T) would give (0.366, 0.634)); draft logits (0, 0) give q = 1/2.
+    # Draft x = 0: ratio = 0.1/0.5 = 0.2; u = 0.25 rejects, u = 0.15 accepts.
+    t = [[0.0, np.log(3.0)], [0.0, 0.0]]
+    d = [[0.0, 0.0]]
+    r = oracle.verify(_explicit(t, d, [0], [[0.25, 0.0], [0.0, 0.0]], 0.5, 1))
+    assert r["num_accepted"][0] == 0 and r["out_tokens"][0] == 1
+    assert r["p_x"][0] == pytest.approx(0.1, rel=1e-6)   # ln 3 is stored as float32
+    r = oracle.verify(_explicit(t, d, [0], [[0.15, 0.0], [0.0, 0.0]], 0.5, 1))
+    assert r["num_accepted"][0] == 1
+
+
+def test_draft_ids_outside_vocabulary_are_rejected():
+    t = [[0, 1, 2], [0, 1, 2], [0, 1, 2]]
+    d = [[0, 1, 2], [0, 1, 2]]
+    for bad in (-1, 3):
+        r = oracle.verify(_explicit(t, d, [2, bad], [[0.0, 0.0], [0.0, 0.9], [0.0, 0.0]],
+                                    1.0, 2))
+        assert r["num_accepted"][0] == 1 and r["out_tokens"][0] == 2
+        assert r["p_x"][1] == 0.0 and r["q_x"][1] == 0.0
+        # p = q at row 1 so the residual is empty: the fallback samples from p
+        assert r["fallback"][0] == 1 and r["out_tokens"][1] == 2
+        rg = oracle.verify(_explicit(t, d, [2, bad], np.zeros((3, 2)), 0.0, 2))
+        assert list(rg["out_tokens"]) == [2, 2, -1]
+
+
+def test_low_temperature_sampling_reduces_to_greedy():
+    # As T -> 0+, p and q tend to one-hot vectors at the argmaxes: acceptance, residual and
+    # bonus all return the target argmax, which is the greedy result.
+    T = 1e-6
+    w = workloads.small(B=200, gamma=5, V=40, dtype="f32", seed=21, temperatures=T,
+                        draft_sigma=0.5)
+    for rows in (w.target, w.draft):     # every row's maximum is clear at this temperature
+        srt = np.sort(workloads.decode(rows, "f32"), axis=1)
+        assert (srt[:, -1] - srt[:, -2]).min() > 50 * T
+    rs = oracle.verify(w)
+    rg = oracle.verify(w, greedy=True)
+    np.testing.assert_array_equal(rs["out_tokens"], rg["out_tokens"])
+    np.testing.assert_array_equal(rs["num_accepted"], rg["num_accepted"])
+
+
+# --------------------------------------------------------------------------- distributions
+
+def test_acceptance_probability_is_min_one_ratio():
+    # Stratified grid of N uniforms: the accepted fraction equals min(1, p(x)/q(x)) to 1/N.
+    V, N = 5, 4000
+    zt = np.array([[0.3, -1.0, 1.2, 0.0, 0.7], [0.0] * V])
+    zd = np.array([[1.0, -0.5, 0.2, 0.4, 0.7]])
+    T = 0.8
+    p, q = _softmax(zt[0], T), _softmax(zd[0], T)
+    grid = ((np.arange(N) + 0.5) / N).astype(np.float32)
+    for x in range(V):
+        w = Workload("grid", "f32", N, 1, V, np.tile(zt.astype(np.float32), (N, 1)),
+                     np.tile(zd.astype(np.float32), (N, 1)), np.full(N, x, np.int32),
+                     _grid_uniforms(grid), np.full(N, T, np.float32))
+        r = oracle.verify(w)
+        frac = (r["num_accepted"] == 1).mean()
+        assert abs(frac - min(1.0, p[x] / q[x])) <= 1.0 / N + 1e-7
+
+
+def _grid_uniforms(grid):
+    """Uniform rows for a gamma = 1 request per grid point: [u, 0.5] then [0.5, 0.5]."""
+    n = len(grid)
+    u = np.full((n, 2, 2), 0.5, dtype=np.float32)
+    u[:, 0, 0] = grid
+    return u.reshape(2 * n, 2)
+
+
+def test_exact_marginal_on_a_stratified_grid():
+    # V = 3, gamma = 1.  For each draft x (weight q(x)) and an N x N stratified grid over
+    # (u_accept, u_sample), the token emitted at position 0 must be distributed as p to
+    # O(1/N): the exactness claim of the pages, without sampling noise.
+    V, N, T = 3, 600, 1.0
+    zt = np.array([[0.2, 1.1, -0.4], [0.0, 0.0, 0.0]])
+    zd = np.array([[0.9, 0.1, 0.3]])
+    p, q = _softmax(zt[0], T), _softmax(zd[0], T)
+    g = ((np.arange(N) + 0.5) / N).astype(np.float32)
+    ua, us = np.meshgrid(g, g, indexing="ij")
+    n = N * N
+    uni = np.full((n, 2, 2), 0.5, dtype=np.float32)
+    uni[:, 0, 0] = ua.ravel()
+    uni[:, 0, 1] = us.ravel()
+    dist = np.zeros(V)
+    for x in range(V):
+        w = Workload("grid2", "f32", n, 1, V, np.tile(zt.astype(np.float32), (n, 1)),
+                     np.tile(zd.astype(np.float32), (n, 1)), np.full(n, x, np.int32),
+                     uni.reshape(2 * n, 2), np.full(n, T, np.float32))
+        r = oracle.verify(w)
+        tok0 = r["out_tokens"].reshape(n, 2)[:, 0]
+        dist += q[x] * np.bincount(tok0, minlength=V) / n
+    np.testing.assert_allclose(dist, p, atol=3.0 / N)
+
+
+def _chi2_trials(seed, V=16, gamma=3, T=0.9, n_total=1_000_000, chunk=250_000):
+    T = float(np.float32(T))
+    rng = np.random.default_rng(seed)
+    zt = rng.normal(0, 1.5, size=(gamma + 1, V))
+    zd = zt[:gamma] + rng.normal(0, 1.0, size=(gamma, V))
+    toks, nacc = [], []
+    for c in range(n_total // chunk):
+        w = workloads.tiled(zt, zd, chunk, T=T, seed=seed * 100 + c)
+        r = oracle.verify(w)
+        toks.append(r["out_tokens"].reshape(chunk, gamma + 1))
+        nacc.append(r["num_accepted"])
+        zt_s = workloads.decode(w.target[: gamma + 1], "f32")
+        zd_s = workloads.decode(w.draft[:gamma], "f32")
+    return np.concatenate(toks), np.concatenate(nacc), zt_s, zd_s, T
+
+
+def test_chi_square_emitted_tokens_follow_p():
+    # 10^6 trials, V = 16, gamma = 3, a different p and q at every position.  Conditional
+    # on reaching position k, the emitted token there must be distributed as p_k (accepted
+    # drafts, residual draws and the bonus together).
+    toks, nacc, zt, zd, T = _chi2_trials(seed=7)
+    gamma = zd.shape[0]
+    for k in range(gamma + 1):
+        reached = nacc >= k
+        assert reached.sum() > 50_000
+        obs = np.bincount(toks[reached, k], minlength=zt.shape[1])
+        pval, x2, df = chi2_pvalue(obs, _softmax(zt[k], T))
+        assert pval > 1e-3, (k, pval, x2, df)
+    # acceptance rate at position 0 is sum_x min(p, q)
+    beta0 = np.minimum(_softmax(zt[0], T), _softmax(zd[0], T)).sum()
+    assert abs((nacc >= 1).mean() - beta0) < 5 * np.sqrt(beta0 * (1 - beta0) / len(nacc))
+
+
+def test_chi_square_residual_follows_p_corr():
+    # Conditional on a rejection at position 0, the replacement follows
+    # max(p - q, 0) / sum max(p - q, 0) (Speculative Decoding wiki, p_corr).
+    toks, nacc, zt, zd, T = _chi2_trials(seed=9)
+    p, q = _softmax(zt[0], T), _softmax(zd[0], T)
+    rej = nacc == 0
+    obs = np.bincount(toks[rej, 0], minlength=zt.shape[1])
+    pval, x2, df = chi2_pvalue(obs, np.maximum(p - q, 0.0))
+    assert pval > 1e-3, (pval, x2, df)
+
+
+def test_worked_example_tokens_per_pass():
+    g = json.loads((GOLDEN / "tokens_per_pass.json").read_text())
+    alpha, gamma = g["alpha"], g["gamma"]
+    closed = (1 - alpha ** (gamma + 1)) / (1 - alpha)
+    assert abs(closed - g["tokens_per_pass_printed"]) <= g["printed_resolution"]
+    accepted_closed = sum(alpha ** k for k in range(1, gamma + 1))
+    assert accepted_closed == pytest.approx(closed - 1, rel=1e-12)
+    # p = (0.9, 0.1), q = (0.7, 0.3) at every position: sum min(p, q) = 0.8 = alpha
+    zt = np.log(np.array([[0.9, 0.1]] * (gamma + 1)))
+    zd = np.log(np.array([[0.7, 0.3]] * gamma))
+    n = 1_000_000
+    w = workloads.tiled(zt, zd, n, T=1.0, seed=31)
+    r = oracle.verify(w)
+    emitted = r["num_accepted"].astype(np.float64) + 1
+    se = emitted.std() / np.sqrt(n)
+    assert abs(emitted.mean() - closed) < 4 * se, (emitted.mean(), closed, se)
+    assert abs(r["num_accepted"].mean() - accepted_closed) < 4 * se
+    assert abs(emitted.mean() - g["tokens_per_pass_printed"]) <= g["printed_resolution"]

@@ -1,0 +1,58 @@
+"""The seeded input generators: encoding, layout and the workloads' shapes."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+
+
+def test_bf16_encoding_matches_torch_round_to_nearest_even():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.normal(0, 3, 100_000), rng.normal(0, 1e-3, 1000),
+                        [0.0, -0.0, 1.0, -2.5, 3.0e38, 1e-40]]).astype(np.float32)
+    ours = workloads.bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    back = workloads.bf16_to_f32(ours)
+    np.testing.assert_array_equal(back, torch.from_numpy(ours.view(np.int16)).view(
+        torch.bfloat16).float().numpy())
+
+
+@pytest.mark.parametrize("cid,shape", [(1, (5, 4, 1000, "f32", 36_000, 4)),
+                                       (2, (48, 40, 32000, "bf16", 3_072_000, 40)),
+                                       (3, (320, 256, 128256, "bf16", 147_750_912, 256))])
+def test_small_workload_shapes_and_compulsory_bytes(cid, shape):
+    R_t, R_d, V, dtype, nbytes, pos = shape
+    w = workloads.config(cid)
+    assert (w.R_t, w.R_d, w.V, w.dtype) == (R_t, R_d, V, dtype)
+    assert w.compulsory_bytes == nbytes and w.positions == pos
+    assert w.uniforms.shape == (R_t, 2) and w.uniforms.dtype == np.float32
+    assert ((w.uniforms >= 0) & (w.uniforms < 1)).all()
+    assert ((w.draft_tokens >= 0) & (w.draft_tokens < V)).all()
+
+
+def test_generation_is_deterministic_and_layout_consistent():
+    a = workloads.small(B=9, gamma=5, V=77, dtype="bf16", seed=4, ragged=True,
+                        temperatures=np.linspace(0, 1, 9))
+    b = workloads.small(B=9, gamma=5, V=77, dtype="bf16", seed=4, ragged=True,
+                        temperatures=np.linspace(0, 1, 9))
+    for f in ("target", "draft", "draft_tokens", "uniforms", "temperatures", "cu_draft"):
+        np.testing.assert_array_equal(getattr(a, f), getattr(b, f))
+    assert a.cu_draft[0] == 0 and a.cu_draft[-1] == a.R_d and a.R_t == a.R_d + a.B
+    np.testing.assert_array_equal(a.target_base, a.cu_draft[:-1] + np.arange(9))
+    # greedy requests' drafts are the draft-row argmax
+    zd = workloads.decode(a.draft, "bf16")
+    for bi in np.flatnonzero(a.temperatures == 0):
+        db, g = a.draft_base[bi], a.gammas[bi]
+        np.testing.assert_array_equal(a.draft_tokens[db: db + g], np.argmax(zd[db: db + g], 1))
+
+
+def test_gumbel_draft_draw_follows_the_tempered_softmax():
+    from scipy import special
+    from tests.stats_util import chi2_pvalue
+    rng = np.random.default_rng(5)
+    z = rng.normal(0, 1.0, 12)
+    toks = workloads.draw_draft_tokens(np.broadcast_to(z, (400_000, 12)), 0.6,
+                                       np.random.default_rng(6))
+    pval, _, _ = chi2_pvalue(np.bincount(toks, minlength=12), special.softmax(z / 0.6))
+    assert pval > 1e-3
