@@ -1,0 +1,203 @@
+"""Benchmark of the speculative-sampling verification step on one MI355X.
+
+One step = one call of spec_verify_sample over a whole batch (row statistics, accept tests,
+first-reject scan, residual mass, draw; greedy rows of the batch included).  Inputs are
+seeded synthetic workloads resident in HBM before timing; consecutive steps rotate over
+enough input copies (> 2 x the 256 MB last-level cache) that no step reads cache-hot logits.
+
+Prints one JSON line: verified positions/s (value), logit GB/s and HBM fraction, the row
+statistics kernel's achieved bandwidth from HIP events recorded on its stream, and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MALL_BYTES = 256 << 20          # last-level (Infinity) cache
+KERNELS = ["k_rowstats", "k_decide", "k_resid", "k_sample"]
+DEFAULT_WORKLOAD = 5
+TRAFFIC_FILE = ROOT / "profiles" / "traffic_k_rowstats.json"
+KERNEL_SRC = ROOT / "speculative_sampling_verification_spec_amd" / "csrc" / "spec_verify.hip"
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime (torch's events only see torch's own
+    stream bookkeeping; these are recorded by the library on the stream it launches on)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            evs.append(e.value)
+        return evs
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a),
+                                        ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def traffic_for_current_kernel():
+    """HBM bytes per k_rowstats launch from the committed rocprofv3 counter runs, or None if
+    the kernel source changed since they were taken."""
+    if not TRAFFIC_FILE.exists():
+        return None
+    rec = json.loads(TRAFFIC_FILE.read_text())
+    sha = hashlib.sha256(KERNEL_SRC.read_bytes()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec
+
+
+def cpu_baseline(w, target_seconds: float):
+    """The oracle, as it stands, on the first n requests of the workload, n sized so the
+    run takes about ``target_seconds`` on this host's cores."""
+    import oracle
+    threads = oracle.max_threads()
+    probe_n = min(w.B, 16)
+    t = time.perf_counter()
+    oracle.verify(w, requests=list(range(probe_n)), threads=threads)
+    dt = time.perf_counter() - t
+    n = int(min(w.B, max(probe_n, probe_n * target_seconds / max(dt, 1e-3))))
+    reqs = list(range(n))
+    t = time.perf_counter()
+    oracle.verify(w, requests=reqs, threads=threads)
+    dt = time.perf_counter() - t
+    positions = int(w.gammas[:n].sum())
+    return {"value": positions / dt, "unit": "positions/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {w.B} requests of the benchmark workload "
+                      f"({positions} positions, {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD,
+                    help="1..5; the JSON line is for workload 5 by default")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this step has no multi-GPU path (asked for "
+              f"--gpus {args.gpus}); per-request sharding across GPUs needs no communication "
+              f"and is described in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+    import speculative_sampling_verification_spec_amd as sv
+
+    torch.cuda.set_device(0)
+    t_gen = time.perf_counter()
+    w = workloads.config(args.workload)
+    print(f"[bench] generated workload {args.workload} in {time.perf_counter() - t_gen:.1f} s",
+          file=sys.stderr, flush=True)
+    nbytes = w.compulsory_bytes
+    copies = max(2, math.ceil(2 * MALL_BYTES / nbytes) + 1)
+    copies = min(copies, max(2, (8 << 30) // max(nbytes, 1)))
+    base = workloads.to_torch(w)
+    inputs = [base] + [dict(base, target=base["target"].clone(), draft=base["draft"].clone())
+                       for _ in range(copies - 1)]
+    code = sv.SPEC_F32 if w.dtype == "f32" else sv.SPEC_BF16
+    ws = sv.alloc_workspace(w.B, w.gamma, w.V, code)
+    out = torch.empty(w.R_t, dtype=torch.int32, device="cuda")
+    nacc = torch.empty(w.B, dtype=torch.int32, device="cuda")
+    hip = HipEvents()
+    n_ev = 8
+    evs = hip.create(n_ev * args.steps)
+    probes = [sv.make_probe(events=evs[n_ev * k: n_ev * (k + 1)]) for k in range(args.steps)]
+
+    def step(k, probe):
+        d = inputs[k % copies]
+        sv.spec_verify_sample(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temps"],
+                              w.gamma, out, nacc, ws, cu_draft=d["cu"], probe=probe)
+
+    for k in range(args.warmup):
+        step(k, None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k, probes[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    per_kernel_us = {}
+    for i, name in enumerate(KERNELS):
+        d = [hip.elapsed_ms(evs[n_ev * k + 2 * i], evs[n_ev * k + 2 * i + 1])
+             for k in range(args.steps)]
+        per_kernel_us[name] = round(1e3 * float(np.mean(d)), 2)
+    hip.destroy(evs)
+
+    rs_us = per_kernel_us["k_rowstats"]
+    achieved = nbytes / (rs_us * 1e-6) / 1e9
+    traffic = traffic_for_current_kernel()
+    positions = w.positions
+    value = positions / (ms_per_step * 1e-3)
+    logit_gbps = nbytes / (ms_per_step * 1e-3) / 1e9
+    result = {
+        "metric": "verified positions/sec and logit GB/s (fraction of HBM peak), 1 MI355X",
+        "value": round(value, 1),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {w.name}", "B": w.B, "gamma_max": w.gamma,
+                   "V": w.V, "logit_dtype": w.dtype, "positions_per_step": positions,
+                   "logit_bytes_per_step": nbytes, "input_copies": copies,
+                   "parallelism": "single GPU"},
+        "logit_GB_per_s": round(logit_gbps, 1),
+        "hbm_frac": round(logit_gbps / HBM_PEAK_GBPS, 4),
+        "kernel_us": per_kernel_us,
+        "roofline": {"bound": "hbm", "kernel": "k_rowstats", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None if traffic is None else traffic["hbm_bytes_per_launch"]},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,149 @@
+/*
+ * spec_verify.h — C ABI of the speculative-sampling verification step on MI355X (gfx950).
+ *
+ * The operation (defined on these pages; cited by title and section):
+ *  - "Speculative Decoding : accélérer l'inférence des LLM" (blent.ai), sections
+ *    "Principe et garanties mathématiques" and "Pourquoi la qualité est préservée":
+ *    a drafted token x is accepted with probability min(1, p(x)/q(x)); the first rejected
+ *    draft is replaced by a draw from max(p - q, 0) renormalised; a step emits between 1 and
+ *    gamma + 1 tokens; at temperature zero a draft is accepted iff it is the target's argmax,
+ *    which replaces it otherwise.
+ *  - "Speculative Decoding — Come Accelerare l'Inferenza LLM di 2-3x" (aimpact), section
+ *    "Il meccanismo": the draft hands over its distribution q for every draft step, the
+ *    target yields p for every position, drafts after the first rejection are discarded.
+ *  - "Speculative Decoding" (haruk1y wiki), section "数式で見る speculative decoding の正しさ":
+ *    the acceptance probability alpha(x) and the correction distribution p_corr.
+ *  - "Accélérer Sonar grâce à la spéculation" (Perplexity), sections "Décodage spéculatif"
+ *    and "Inférence avec le décodage spéculatif": the longest acceptable prefix is kept, the
+ *    target's logits at the mismatch or after the last draft are sampled for one more token,
+ *    and the accepted length feeds the next step (so it stays on the device here).
+ *
+ * Conventions fixed by this library where the pages leave a step open:
+ *  - p = softmax(z_target / T_b), q = softmax(z_draft / T_b), one temperature per request;
+ *    a request is sampled iff T_b > 0, greedy otherwise (T = 0 exactly is the pages' case).
+ *    Temperatures below about 1.4e-38 act as that value.
+ *  - uniforms[r][0] is the accept test at draft position r (accept iff u < p(x)/q(x),
+ *    strictly); uniforms[r][1] is the draw for the token emitted at target row r, used only
+ *    at the stop row: the residual after a rejection, or the bonus from p at row gamma_b.
+ *  - The draw is an inverse CDF in vocabulary order over unnormalised weights r_k:
+ *    k* = min { k : r_k > 0 and C_k > u * R }, C_k the running sum, R the total.
+ *  - Greedy argmax ties resolve to the lowest index.  A draft id outside [0, V) has
+ *    p(x) = q(x) = 0 and is rejected.
+ *
+ * Layout.  All logits are row-major with row stride V elements.  Request b has gamma_b
+ * drafts; gamma_b = gamma when cu_draft is NULL (dense), else cu_draft[b+1] - cu_draft[b]
+ * (CSR over draft rows, 0 <= gamma_b <= gamma).  Request b's draft rows and draft tokens
+ * start at cu_draft[b] (dense: b*gamma); its target rows, uniform rows and output slots start
+ * at cu_draft[b] + b (dense: b*(gamma+1)).  R_t = total target rows = R_d + B.
+ *
+ * Ownership.  The caller allocates and owns every buffer (device memory unless stated),
+ * including the workspace.  The library allocates nothing, keeps no state between calls,
+ * is reentrant for distinct workspaces, and touches only the ranges described.  Calls are
+ * asynchronous on `stream` (a hipStream_t; NULL is the null stream) and never wait for the
+ * device.  Two calls may share a workspace only when ordered on one stream.
+ *
+ * Errors.  Every entry point returns SPEC_OK (0) or a negative code; arguments are checked
+ * on the host before anything is enqueued, so an argument error leaves outputs untouched.
+ * SPEC_ERR_HIP means a kernel launch failed; kernels of the same call launched before it
+ * stay enqueued.  Device data are not checked (that would need a sync): logits must be
+ * finite, cu_draft a valid CSR whose rows exist, uniforms in [0, 1).
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
+
+enum {
+  SPEC_OK = 0,
+  SPEC_ERR_NULL = -1,       /* a required pointer is NULL                                */
+  SPEC_ERR_SHAPE = -2,      /* B < 0, gamma not in [0, 64], V not in [1, 2^31 - 1], or a
+                               grid too large                                            */
+  SPEC_ERR_DTYPE = -3,      /* dtype is not a spec_dtype                                 */
+  SPEC_ERR_WORKSPACE = -4,  /* workspace smaller than spec_verify_workspace_size, or not
+                               256-byte aligned                                          */
+  SPEC_ERR_HIP = -5         /* a kernel launch or event record failed                    */
+};
+
+/* Largest gamma (drafts per request) the kernels take. */
+#define SPEC_MAX_GAMMA 64
+
+/*
+ * Optional diagnostics.  Every pointer may be NULL; all are device pointers except
+ * `events`.  Entries of greedy requests are written only where stated.
+ */
+typedef struct spec_probe {
+  double *p_x;        /* [R_d] p_i(x_i) at each draft position of sampled requests         */
+  double *q_x;        /* [R_d] q_i(x_i)                                                    */
+  float *row_max_t;   /* [R_t] max raw logit of each target row (greedy requests too)      */
+  double *row_sum_t;  /* [R_t] sum_k exp((z_k - max) / T_b), sampled requests              */
+  float *row_max_d;   /* [R_d] max raw logit of each draft row read (sampled requests)     */
+  double *row_sum_d;  /* [R_d] as row_sum_t for draft rows                                 */
+  double *resid_mass; /* [B] total probability mass of the distribution drawn from at the
+                         stop row: sum_k max(p_k - q_k, 0) after a rejection, sum_k p_k
+                         (= 1) for the bonus; sampled requests                            */
+  void *events[8];    /* host: hipEvent_t or NULL; events[2k] / events[2k+1] are recorded on
+                         `stream` just before / after the k-th kernel launch of the call
+                         (sample: 0 row statistics, 1 decide, 2 residual, 3 draw;
+                          greedy: 0 row argmax, 1 decide)                                */
+} spec_probe;
+
+/*
+ * spec_verify_sample — verify gamma drafts per request and emit the step's tokens.
+ *
+ *  target_logits  [R_t, V] dtype   p's logits at positions 0..gamma_b of each request
+ *  draft_logits   [R_d, V] dtype   q's logits at draft positions 0..gamma_b-1
+ *  dtype          SPEC_F32 or SPEC_BF16, for both logit arrays
+ *  draft_tokens   [R_d] int32      the drafted ids x_i
+ *  uniforms       [R_t, 2] float   see the conventions above
+ *  temperatures   [B] float        T_b; T_b > 0 samples, otherwise greedy (draft logits of a
+ *                                  greedy request are never read)
+ *  B, gamma       requests; drafts per request (dense) or the largest gamma_b (CSR)
+ *  cu_draft       [B+1] int32 or NULL
+ *  V              vocabulary size
+ *  out_tokens     [R_t] int32      request b's slots 0..gamma_b: the n_b accepted drafts, the
+ *                                  token emitted at the stop row n_b, then -1
+ *  out_num_accepted [B] int32      n_b in [0, gamma_b]; the step emits n_b + 1 tokens
+ *  workspace      device scratch of at least spec_verify_workspace_size(B, gamma, V, dtype)
+ *                 bytes, 256-byte aligned; no initial contents are required
+ *  probe          NULL, or diagnostics as above
+ *  stream         hipStream_t
+ *
+ * B == 0 is an empty call: SPEC_OK, nothing enqueued, pointers unchecked.
+ */
+int spec_verify_sample(const void *target_logits, const void *draft_logits, int dtype,
+                       const int32_t *draft_tokens, const float *uniforms,
+                       const float *temperatures, int32_t B, int32_t gamma,
+                       const int32_t *cu_draft, int64_t V, int32_t *out_tokens,
+                       int32_t *out_num_accepted, void *workspace, size_t workspace_bytes,
+                       const spec_probe *probe, void *stream);
+
+/*
+ * spec_verify_greedy — the temperature-zero step (blent.ai page, "Pourquoi la qualité est
+ * préservée"; wiki page, "実装上の注意"): draft i is accepted iff it equals the lowest-index
+ * argmax of target row i; the argmax at the stop row is emitted.  Draft logits are not
+ * taken.  Arguments as for spec_verify_sample; probe fields other than row_max_t and events
+ * are ignored.
+ */
+int spec_verify_greedy(const void *target_logits, int dtype, const int32_t *draft_tokens,
+                       int32_t B, int32_t gamma, const int32_t *cu_draft, int64_t V,
+                       int32_t *out_tokens, int32_t *out_num_accepted, void *workspace,
+                       size_t workspace_bytes, const spec_probe *probe, void *stream);
+
+/* Workspace bytes needed by either entry point for these sizes; 0 for invalid sizes. */
+size_t spec_verify_workspace_size(int32_t B, int32_t gamma, int64_t V, int dtype);
+
+/* Static description of a return code. */
+const char *spec_verify_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,181 @@
+"""Python binding of ``libspecverify.so`` (the C ABI in ``include/spec_verify.h``).
+
+Argument marshalling only: every step of the verification runs in the library's HIP
+kernels.  Functions carry the C names and take torch tensors on the GPU; torch supplies
+device memory and the current stream, nothing else.  If the library has not been built the
+import still succeeds, but every call raises: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+from typing import Optional
+
+_PKG = Path(__file__).resolve().parent
+LIB_PATH = _PKG / "libspecverify.so"
+
+SPEC_F32, SPEC_BF16 = 0, 1
+SPEC_MAX_GAMMA = 64
+SPEC_OK = 0
+
+_lib = None
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {spec_verify_strerror(code)} (code {code})")
+        self.code = code
+
+
+class _Probe(ctypes.Structure):
+    _fields_ = [("p_x", ctypes.c_void_p), ("q_x", ctypes.c_void_p),
+                ("row_max_t", ctypes.c_void_p), ("row_sum_t", ctypes.c_void_p),
+                ("row_max_d", ctypes.c_void_p), ("row_sum_d", ctypes.c_void_p),
+                ("resid_mass", ctypes.c_void_p), ("events", ctypes.c_void_p * 8)]
+
+
+def lib():
+    """Load the HIP library; raises if it is missing (build it with ``build.build()``)."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build the HIP library first "
+                "(python -m speculative_sampling_verification_spec_amd.build)")
+        L = ctypes.CDLL(str(LIB_PATH))
+        P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.spec_verify_sample.restype = ctypes.c_int
+        L.spec_verify_sample.argtypes = [P, P, ctypes.c_int, P, P, P, i32, i32, P, i64, P, P,
+                                         P, sz, P, P]
+        L.spec_verify_greedy.restype = ctypes.c_int
+        L.spec_verify_greedy.argtypes = [P, ctypes.c_int, P, i32, i32, P, i64, P, P, P, sz, P,
+                                         P]
+        L.spec_verify_workspace_size.restype = sz
+        L.spec_verify_workspace_size.argtypes = [i32, i32, i64, ctypes.c_int]
+        L.spec_verify_strerror.restype = ctypes.c_char_p
+        L.spec_verify_strerror.argtypes = [ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def spec_verify_strerror(code: int) -> str:
+    return lib().spec_verify_strerror(int(code)).decode()
+
+
+def spec_verify_workspace_size(B: int, gamma: int, V: int, dtype: int) -> int:
+    return int(lib().spec_verify_workspace_size(int(B), int(gamma), int(V), int(dtype)))
+
+
+# ----------------------------------------------------------------------------- torch glue
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    if t.dtype == torch.bfloat16:
+        return SPEC_BF16
+    raise ValueError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _dev(t, name, dtype=None, numel=None):
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_probe(p_x=None, q_x=None, row_max_t=None, row_sum_t=None, row_max_d=None,
+               row_sum_d=None, resid_mass=None, events=None) -> _Probe:
+    """Diagnostics struct; tensors (device) or None, ``events`` a list of up to 8 raw
+    hipEvent_t handles (ints) or None."""
+    pr = _Probe()
+    torch = _torch()
+    for name, t, dt in (("p_x", p_x, torch.float64), ("q_x", q_x, torch.float64),
+                        ("row_max_t", row_max_t, torch.float32),
+                        ("row_sum_t", row_sum_t, torch.float64),
+                        ("row_max_d", row_max_d, torch.float32),
+                        ("row_sum_d", row_sum_d, torch.float64),
+                        ("resid_mass", resid_mass, torch.float64)):
+        p = _dev(t, name, dt)
+        setattr(pr, name, p.value if p is not None else None)
+    for i, e in enumerate(events or []):
+        pr.events[i] = e
+    return pr
+
+
+def _check(rc: int, where: str):
+    if rc != SPEC_OK:
+        raise SpecVerifyError(rc, where)
+
+
+def spec_verify_sample(target_logits, draft_logits, draft_tokens, uniforms, temperatures,
+                       gamma: int, out_tokens, out_num_accepted, workspace,
+                       cu_draft=None, probe: Optional[_Probe] = None, stream=None) -> None:
+    """Asynchronous on the current (or given) stream.  ``target_logits [R_t, V]`` and
+    ``draft_logits [R_d, V]`` share one dtype (float32 / bfloat16); ``B`` is
+    ``temperatures.numel()``; ``workspace`` is a uint8 tensor of at least
+    ``spec_verify_workspace_size`` bytes."""
+    torch = _torch()
+    B = temperatures.numel()
+    V = target_logits.shape[-1]
+    dt = dtype_code(target_logits)
+    if draft_logits.dtype != target_logits.dtype:
+        raise ValueError("target and draft logits must share a dtype")
+    rc = lib().spec_verify_sample(
+        _dev(target_logits, "target_logits"), _dev(draft_logits, "draft_logits"), dt,
+        _dev(draft_tokens, "draft_tokens", torch.int32),
+        _dev(uniforms, "uniforms", torch.float32),
+        _dev(temperatures, "temperatures", torch.float32), B, int(gamma),
+        _dev(cu_draft, "cu_draft", torch.int32, B + 1), V,
+        _dev(out_tokens, "out_tokens", torch.int32),
+        _dev(out_num_accepted, "out_num_accepted", torch.int32, B),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        None if probe is None else ctypes.byref(probe), _stream(stream))
+    _check(rc, "spec_verify_sample")
+
+
+def spec_verify_greedy(target_logits, draft_tokens, gamma: int, out_tokens,
+                       out_num_accepted, workspace, cu_draft=None,
+                       probe: Optional[_Probe] = None, stream=None) -> None:
+    """Temperature-zero verification; ``B`` is ``out_num_accepted.numel()``."""
+    torch = _torch()
+    B = out_num_accepted.numel()
+    V = target_logits.shape[-1]
+    rc = lib().spec_verify_greedy(
+        _dev(target_logits, "target_logits"), dtype_code(target_logits),
+        _dev(draft_tokens, "draft_tokens", torch.int32), B, int(gamma),
+        _dev(cu_draft, "cu_draft", torch.int32, B + 1), V,
+        _dev(out_tokens, "out_tokens", torch.int32),
+        _dev(out_num_accepted, "out_num_accepted", torch.int32, B),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        None if probe is None else ctypes.byref(probe), _stream(stream))
+    _check(rc, "spec_verify_greedy")
+
+
+def alloc_workspace(B: int, gamma: int, V: int, dtype: int, device="cuda"):
+    """uint8 device tensor of the size the library asks for (torch's allocations are
+    256-byte aligned)."""
+    torch = _torch()
+    n = spec_verify_workspace_size(B, gamma, V, dtype)
+    if n == 0:
+        raise ValueError("invalid sizes for spec_verify")
+    return torch.empty(n, dtype=torch.uint8, device=device)

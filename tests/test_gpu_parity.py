@@ -1,0 +1,238 @@
+"""HIP path vs the fp64 oracle on the same seeded inputs, through the C ABI.
+
+Small shapes run the oracle on every request; the two largest workloads run on the GPU at
+full size, in the launch configuration the benchmark times, with the oracle computing a
+spread sample of requests and every request checked for the invariants.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests import parity
+from tests.gpu_run import run, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _both(w, greedy=False, requests=None):
+    print(f"[gpu] {w.name} B={w.B} gamma={w.gamma} V={w.V} {w.dtype} greedy={greedy}",
+          flush=True)
+    g = run(w, greedy=greedy)
+    o = oracle.verify(w, requests=requests, greedy=greedy)
+    rep = parity.compare(w, g, o, requests=requests, greedy_call=greedy)
+    print(f"[gpu]   {rep}", flush=True)
+    return g, o, rep
+
+
+# ----------------------------------------------------------------------- small shapes
+
+SMALL = [
+    # (B, gamma, V, dtype, ragged, temps)      V spans: odd (element loads), one tile,
+    (3, 4, 37, "f32", False, 1.0),           # several tiles with a ragged tail
+    (5, 3, 1000, "bf16", True, 0.7),
+    (4, 6, 4099, "f32", True, "mixed"),
+    (6, 5, 16392, "bf16", False, "mixed"),
+    (7, 8, 50000, "f32", True, "mixed"),
+    (9, 4, 33001, "bf16", True, "mixed"),
+    (2, 2, 131072 + 8, "bf16", False, 1.3),
+    (3, 7, 100003, "f32", False, 0.9),
+]
+
+
+@pytest.mark.parametrize("B,gamma,V,dtype,ragged,temps", SMALL)
+def test_small_shapes_match_oracle(B, gamma, V, dtype, ragged, temps):
+    if temps == "mixed":
+        temps = np.where(np.arange(B) % 3 == 0, 0.0, np.linspace(0.2, 1.5, B))
+    w = workloads.small(B=B, gamma=gamma, V=V, dtype=dtype, seed=B * 1000 + V, ragged=ragged,
+                        temperatures=temps, draft_sigma=0.8)
+    _both(w)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [64, 5000, 40000])
+def test_greedy_entry_point_matches_oracle(dtype, V):
+    w = workloads.small(B=11, gamma=6, V=V, dtype=dtype, seed=V, ragged=True,
+                        temperatures=0.0, draft_sigma=0.3)
+    _both(w, greedy=True)
+    _both(w.as_greedy(), greedy=False)   # T = 0 rows inside the sampling entry point
+
+
+def test_many_requests_peaked_rows():
+    w = workloads.small(B=96, gamma=4, V=8192, dtype="bf16", seed=77, temperatures=0.7,
+                        target_sigma=3.0, draft_sigma=1.0, peaks=5)
+    _, _, rep = _both(w)
+    assert rep["ambiguous"] <= 0.1 * rep["sampled"]
+
+
+# ----------------------------------------------------------------------- edge cases
+
+def test_p_equal_q_accepts_everything_on_gpu():
+    w = workloads.small(B=40, gamma=8, V=3000, dtype="bf16", seed=5, temperatures=0.9,
+                        ragged=True)
+    for b, (tb, db, g) in enumerate(zip(w.target_base, w.draft_base, w.gammas)):
+        w.draft[db: db + g] = w.target[tb: tb + g]
+    rng = np.random.default_rng(9)
+    w.draft_tokens[:] = workloads.draw_draft_tokens(workloads.decode(w.draft, "bf16"), 0.9, rng)
+    w.uniforms[:, 0] = np.float32(np.nextafter(np.float32(1), np.float32(0)))
+    g = run(w)
+    np.testing.assert_array_equal(g["num_accepted"], w.gammas)
+    _both(w)
+
+
+def test_gamma_zero_and_max_gamma():
+    w0 = workloads.small(B=4, gamma=1, V=500, seed=1)
+    # one unused draft row and token keep the (never read) pointers non-NULL
+    w0 = workloads.Workload("gamma0", "f32", 4, 0, 500, w0.target[:4].copy(),
+                            np.zeros((1, 500), np.float32), np.zeros(1, np.int32),
+                            w0.uniforms[:4].copy(), np.array([1.0, 0.0, 0.5, 2.0], np.float32))
+    _both(w0)
+    w64 = workloads.small(B=3, gamma=64, V=300, dtype="f32", seed=2, temperatures=1.0,
+                          draft_sigma=0.05)
+    g, o, _ = _both(w64)
+    assert (o["num_accepted"] >= 32).any()  # long accepted runs exercise the lane loop
+    wg = workloads.small(B=3, gamma=64, V=300, dtype="bf16", seed=3, temperatures=0.0,
+                         draft_sigma=0.0)
+    g, o, _ = _both(wg, greedy=True)
+    assert (o["num_accepted"] == 64).all()   # drafts are the target argmax: all accepted
+
+
+def test_ragged_with_empty_requests():
+    base = workloads.small(B=6, gamma=5, V=777, dtype="bf16", seed=4, ragged=True,
+                           temperatures=np.array([0.8, 0, 1.1, 0.5, 0, 0.3]))
+    # make requests 1 and 4 have no drafts: drop their draft rows and rebuild CSR
+    g = base.gammas.copy()
+    keep_d = np.ones(base.R_d, bool)
+    keep_t = np.ones(base.R_t, bool)
+    for b in (1, 4):
+        db, tb = base.draft_base[b], base.target_base[b]
+        keep_d[db: db + g[b]] = False
+        keep_t[tb + 1: tb + g[b] + 1] = False
+        g[b] = 0
+    cu = np.concatenate([[0], np.cumsum(g)]).astype(np.int32)
+    w = workloads.Workload("empty-requests", "bf16", 6, int(g.max()), 777,
+                           base.target[keep_t].copy(), base.draft[keep_d].copy(),
+                           base.draft_tokens[keep_d].copy(), base.uniforms[keep_t].copy(),
+                           base.temperatures.copy(), cu)
+    _both(w)
+
+
+def test_single_token_vocabulary():
+    w = workloads.small(B=5, gamma=3, V=1, dtype="f32", seed=6, ragged=True,
+                        temperatures=np.array([1.0, 0.0, 0.5, 0.0, 2.0]))
+    g, o, _ = _both(w)
+    np.testing.assert_array_equal(g["num_accepted"], w.gammas)
+
+
+def test_extreme_temperatures():
+    temps = np.array([1e-30, 1e-6, 1e-3, 50.0, 1e4, 0.0], dtype=np.float32)
+    w = workloads.small(B=6, gamma=4, V=2048, dtype="bf16", seed=8, temperatures=temps)
+    _both(w)
+
+
+def test_draft_ids_outside_vocabulary():
+    w = workloads.small(B=6, gamma=4, V=900, dtype="f32", seed=10,
+                        temperatures=np.array([1.0, 0.0, 0.6, 0.0, 1.2, 0.9]))
+    w.draft_tokens[1::3] = 900
+    w.draft_tokens[2::5] = -3
+    _both(w)
+    _both(w, greedy=True)
+
+
+def test_unaligned_rows_take_the_element_path():
+    # a row stride that is not a multiple of 16 bytes, and a base offset by one element
+    import torch
+    w = workloads.small(B=4, gamma=3, V=1001, dtype="bf16", seed=12, temperatures=0.9)
+    o = oracle.verify(w)
+    d = to_device(w)
+    for k in ("target", "draft"):
+        t = d[k]
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
+        buf[1:] = t.reshape(-1)
+        d[k] = buf[1:].view_as(t)
+    g = run(w, dev=d)
+    parity.compare(w, g, o)
+
+
+def test_bonus_fallback_when_residual_is_empty():
+    # p = q at a rejected position (uniform at its upper edge): the residual is empty and
+    # the draw falls back to p, as the oracle does.
+    w = workloads.small(B=3, gamma=2, V=256, dtype="f32", seed=13, temperatures=1.0)
+    w.draft[:] = w.target[np.concatenate([[0, 1], [3, 4], [6, 7]])]
+    w.uniforms[:, 0] = 1.0
+    g, o, _ = _both(w)
+    assert (o["fallback"] == 1).all()
+    sure = o["cdf_gap"] >= parity.AMBIGUOUS
+    assert sure.any()
+    for b in np.flatnonzero(sure):
+        tb = w.target_base[b]
+        np.testing.assert_array_equal(g["out_tokens"][tb: tb + 3], o["out_tokens"][tb: tb + 3])
+
+
+# ----------------------------------------------------------------------- the workloads
+
+def test_workload1_tiny_sampling():
+    w = workloads.config(1)
+    g, o, rep = _both(w)
+    assert rep["ambiguous"] == 0
+
+
+def test_workload2_greedy_bit_exact():
+    w = workloads.config(2)
+    g, o, _ = _both(w, greedy=True)
+    g2, _, _ = _both(w, greedy=False)    # the same step through the mixed entry point
+    np.testing.assert_array_equal(g["out_tokens"], g2["out_tokens"])
+
+
+def test_workload3_llama3_vocab_sampling():
+    w = workloads.config(3)
+    _, _, rep = _both(w)
+    assert rep["sampled"] == 64
+
+
+def _spread(B, n):
+    return sorted(set(np.linspace(0, B - 1, n).astype(int).tolist()))
+
+
+def test_workload4_full_size_sampled_requests():
+    w = workloads.config(4)
+    _both(w, requests=_spread(w.B, 48))
+
+
+def test_workload5_full_size_sampled_requests():
+    w = workloads.config(5)
+    _, _, rep = _both(w, requests=_spread(w.B, 96))
+    assert rep["greedy"] > 0 and rep["sampled"] > 0
+
+
+def test_repeated_calls_are_bit_identical():
+    w = workloads.small(B=32, gamma=6, V=20000, dtype="bf16", seed=14, ragged=True,
+                        temperatures=np.linspace(0, 1.2, 32))
+    d = to_device(w)
+    a = run(w, dev=d)
+    b = run(w, dev=d)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+# ----------------------------------------------------------------------- distribution
+
+def test_gpu_chi_square_emitted_tokens_follow_p():
+    from scipy import special
+    from tests.stats_util import chi2_pvalue
+    rng = np.random.default_rng(17)
+    V, gamma, T = 16, 3, 0.9
+    zt = rng.normal(0, 1.5, size=(gamma + 1, V))
+    zd = zt[:gamma] + rng.normal(0, 1.0, size=(gamma, V))
+    n = 1_000_000
+    w = workloads.tiled(zt, zd, n, T=T, seed=170)
+    g = run(w, probe=False)
+    toks = g["out_tokens"].reshape(n, gamma + 1)
+    nacc = g["num_accepted"]
+    zt_s = workloads.decode(w.target[: gamma + 1], "f32")
+    T32 = float(np.float32(T))
+    for k in range(gamma + 1):
+        reached = nacc >= k
+        obs = np.bincount(toks[reached, k], minlength=V)
+        pval, x2, df = chi2_pvalue(obs, special.softmax(zt_s[k] / T32))
+        assert pval > 1e-3, (k, pval, x2, df)

@@ -257,6 +257,25 @@ def config(cid: int) -> Workload:
     raise ValueError(f"no workload {cid}")
 
 
+def to_torch(w: Workload, device="cuda") -> dict:
+    """Copy a workload's arrays to ``device`` as torch tensors (bf16 bits reinterpreted as
+    torch.bfloat16)."""
+    import torch
+
+    def logits(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+        return torch.from_numpy(a).to(device)
+
+    def ints(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(device)
+
+    return dict(target=logits(w.target), draft=logits(w.draft), tokens=ints(w.draft_tokens),
+                uniforms=torch.from_numpy(np.ascontiguousarray(w.uniforms, np.float32)).to(device),
+                temps=torch.from_numpy(np.ascontiguousarray(w.temperatures, np.float32)).to(device),
+                cu=ints(w.cu_draft))
+
+
 def draw_draft_tokens(zd: np.ndarray, T: float, rng: np.random.Generator) -> np.ndarray:
     """Vectorised draft-model draw for rows ``zd [..., V]`` (float64): Gumbel-max at T > 0,
     lowest-index argmax at T = 0."""
