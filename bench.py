@@ -28,7 +28,7 @@ sys.path.insert(0, str(ROOT))
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MALL_BYTES = 256 << 20          # last-level (Infinity) cache
-KERNELS = ["k_rowstats", "k_decide", "k_resid", "k_sample"]
+KERNELS = ["k_rowstats", "k_resid", "k_draw"]
 DEFAULT_WORKLOAD = 5
 TRAFFIC_FILE = ROOT / "profiles" / "traffic_k_rowstats.json"
 KERNEL_SRC = ROOT / "speculative_sampling_verification_spec_amd" / "csrc" / "spec_verify.hip"
@@ -136,7 +136,7 @@ def main():
     out = torch.empty(w.R_t, dtype=torch.int32, device="cuda")
     nacc = torch.empty(w.B, dtype=torch.int32, device="cuda")
     hip = HipEvents()
-    n_ev = 8
+    n_ev = 2 * len(KERNELS)
     evs = hip.create(n_ev * args.steps)
     probes = [sv.make_probe(events=evs[n_ev * k: n_ev * (k + 1)]) for k in range(args.steps)]
 

@@ -37,8 +37,9 @@
  * at cu_draft[b] + b (dense: b*(gamma+1)).  R_t = total target rows = R_d + B.
  *
  * Ownership.  The caller allocates and owns every buffer (device memory unless stated),
- * including the workspace.  The library allocates nothing, keeps no state between calls,
- * is reentrant for distinct workspaces, and touches only the ranges described.  Calls are
+ * including the workspace.  The library allocates nothing and keeps nothing between calls
+ * except, per device, the size of its persistent grid (a property of the device and the
+ * kernel); it is reentrant for distinct workspaces and touches only the ranges described.  Calls are
  * asynchronous on `stream` (a hipStream_t; NULL is the null stream) and never wait for the
  * device.  Two calls may share a workspace only when ordered on one stream.
  *
@@ -63,7 +64,7 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
 enum {
   SPEC_OK = 0,
   SPEC_ERR_NULL = -1,       /* a required pointer is NULL                                */
-  SPEC_ERR_SHAPE = -2,      /* B < 0, gamma not in [0, 64], V not in [1, 2^31 - 1], or a
+  SPEC_ERR_SHAPE = -2,      /* B < 0, gamma not in [0, 64], V not in [1, 2^24], or a
                                grid too large                                            */
   SPEC_ERR_DTYPE = -3,      /* dtype is not a spec_dtype                                 */
   SPEC_ERR_WORKSPACE = -4,  /* workspace smaller than spec_verify_workspace_size, or not
@@ -90,7 +91,7 @@ typedef struct spec_probe {
                          (= 1) for the bonus; sampled requests                            */
   void *events[8];    /* host: hipEvent_t or NULL; events[2k] / events[2k+1] are recorded on
                          `stream` just before / after the k-th kernel launch of the call
-                         (sample: 0 row statistics, 1 decide, 2 residual, 3 draw;
+                         (sample: 0 row statistics, 1 decide + residual sums, 2 draw;
                           greedy: 0 row argmax, 1 decide)                                */
 } spec_probe;
 

@@ -5,68 +5,77 @@
 // and emit a draw from max(p_j - q_j, 0) there, or from p_gamma when nothing was rejected;
 // at temperature zero, compare each draft with the target argmax instead.
 //
-// Four launches on the caller's stream, none of which waits for the host:
-//   1. k_rowstats  — the HBM-bound stream over every needed logit row, split along V.  Each
-//                    workgroup reads one V-slice of one row with 16-byte loads and reduces
-//                    it to (max, sum_k 2^((z_k - max) c)) with c = log2(e)/T (online max,
-//                    fp32 terms, fp64 sums), or to (max, lowest argmax) for greedy rows.
-//   2. k_decide    — one wavefront per request: merges the slice partials in fp64, gathers
-//                    the two logits at each draft token, runs the accept tests lane-parallel
-//                    and finds the first rejection with a ballot + find-first-set.
-//   3. k_resid     — re-reads only the stop row(s) of each sampled request and sums the
-//                    residual weights max(p - q, 0) (or p for the bonus) per V-slice.
-//   4. k_sample    — one workgroup per sampled request: scans the slice sums, then runs a
-//                    block prefix scan inside the chosen slice to find the drawn token.
+// Three launches on the caller's stream, none of which waits for the host:
 //
-// Numerics: every logit is converted exactly to fp32; per-element exponent arguments use
-// the exact difference to the running max and a two-float split of c, so the tempered
-// softmax is not shifted by rounding c; sums across elements, lanes, waves and slices are
-// fp64.  The accept test and p(x), q(x) are evaluated in fp64 from the gathered logits.  The
-// residual weight is computed as p_k (1 - 2^delta_k), delta_k = log2(q_k / p_k) formed in
-// fp64, with expm1 for the bracket: it keeps its relative accuracy when p_k and q_k almost
-// cancel.
+//  k_rowstats  The HBM-bound stream.  Every needed logit row is read exactly once, cut into
+//              16K-element tiles, one workgroup per (row slot, slice) on a 2-D grid; slots a
+//              request does not use exit at once.  The workgroup loads its tile with 16-byte
+//              nontemporal loads straight into registers, takes the tile maximum (wave
+//              shuffles + one LDS exchange), then sums 2^((z - M) c), c = log2(e)/T, with fp32
+//              terms added pairwise per 16-byte unit and fp64 accumulation.  Greedy rows
+//              (T = 0) reduce to (max, lowest argmax).  Output: one partial per (row, slice).
+//
+//  k_resid     Workgroups (request, residual slice).  Each merges its request's row partials
+//              (one wavefront per row, one lane per slice, fp64), runs the accept tests
+//              lane-parallel (p(x), q(x) in fp64 from the two gathered logits) and finds the
+//              first rejection with ballot + find-first-set; slice 0 writes the outputs.  A
+//              sampled request's workgroups then stream their slice of the stop row(s) again
+//              and write one fp64 sum of S_t (p_k - q_k)_+ (or S_t p_k for the bonus) per
+//              64-unit chunk.
+//
+//  k_draw      One workgroup per sampled request: a block scan over the chunk sums picks the
+//              chunk holding u * R, a wavefront scan over its 64 units picks the unit, and a
+//              walk over the unit's elements gives the token.
+//
+// Numerics: logits convert exactly to fp32; exponent arguments carry the temperature as a
+// two-float constant, so rounding never shifts the temperature, and their shifts are kept
+// exact in fp64 when partials are combined; every sum beyond a 16-byte unit is fp64.  Merged
+// row sums are the oracle's normaliser sum_k exp((z_k - max)/T).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <type_traits>
 
 #include "spec_verify.h"
 
 namespace {
 
-constexpr int kThreads = 256;            // 4 wavefronts of 64
+constexpr int kThreads = 256;                // 4 wavefronts of 64
 constexpr int kWaves = kThreads / 64;
-constexpr int kUnroll = 8;               // 16-byte load units in flight per thread
-constexpr int kMaxSplits = 64;
-constexpr int kMinUnitsPerSplit = 64;
-constexpr int kTargetWorkgroups = 2048;  // 8 per CU on 256 CUs
+constexpr int64_t kTileElems = 16384;        // k_rowstats tile: 64 elements per thread
+constexpr int kMaxSlices = 64;               // finest cut of rows in small problems
+constexpr int kSmallGrid = 1024;             // below this many tiles, cut rows finer
+constexpr int kResidGrid = 2048;             // k_resid workgroups aimed for
+constexpr int64_t kMaxGridY = 65535;         // k_rowstats slots per grid row (y), z covers more
+constexpr int kResChunksInFlight = 8;        // 64-unit chunks per wavefront per iteration
+constexpr int64_t kMaxV = int64_t(1) << 24;
 constexpr double kLog2e = 1.4426950408889634074;
-constexpr double kLn2 = 0.69314718055994530942;
 constexpr size_t kAlign = 256;
 
-enum : int32_t { kModeNone = 0, kModeResidual = 1, kModeBonus = 2 };
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Per (row, V-slice) result of k_rowstats.  Sampled rows: m = raw max, s = sum of
-// 2^((z - m) c).  Greedy rows: m = raw max, idx = lowest index attaining it.
+
+// Per (row, V-slice) result of k_rowstats.  Sampled rows: m = raw max of the slice,
+// s = sum of 2^((z - m) c).  Greedy rows: m = raw max, idx = lowest index attaining it.
 struct alignas(16) Partial {
   float m;
   int32_t idx;
   double s;
 };
 
-// Per request, written by k_decide for k_resid / k_sample.
-struct alignas(64) Stop {
-  int32_t j;      // stop row = accepted count
-  int32_t mode;   // kModeNone (greedy), kModeResidual, kModeBonus
-  float mt, md;   // raw maxima of target / draft row j
-  double st, sd;  // their normalisers sum 2^((z - m) c)
-  double c;       // log2(e) / T as the exact sum c_hi + c_lo
-  double k;       // (mt - md) c + log2(st / sd): log2(q_k/p_k) = (zd_k - zt_k) c + k
-  float c_hi, c_lo;
-  int32_t pad[2];
+enum : int32_t { kModeNone = 0, kModeResidual = 1, kModeBonus = 2 };
+
+// The stop row of a sampled request, written by k_resid for k_draw.
+struct alignas(16) Stop {
+  int32_t j, mode;
+  float mt, md;              // raw maxima of target / draft row j
+  float c_hi, c_lo;          // log2(e)/T as a two-float constant
+  float rho_hi, rho_lo;      // S_t / S_d as a two-float constant
+  double st;                 // S_t
+  double pad;
 };
-static_assert(sizeof(Stop) == 64, "Stop layout");
 
 struct Params {
   const void *target, *draft;
@@ -78,18 +87,18 @@ struct Params {
   int32_t *out_tokens, *out_n;
   Partial *parts;
   Stop *stop;
-  double *rsum;
-  int32_t spr;          // row slots per request: 2*gamma+1 (sample) or gamma+1 (greedy)
-  int32_t nsplit;       // V-slices per row in k_rowstats
-  int64_t split_len;    // elements per slice (multiple of the load width)
-  int32_t nsplit_r;     // V-slices per stop row in k_resid
-  int64_t split_len_r;
+  double *chunk_sums;       // [B][chunk_stride] residual sums per 64-unit chunk
+  int64_t chunk_stride;
+  int32_t spr;              // row slots per request: 2*gamma+1 (sample) or gamma+1 (greedy)
+  int32_t nsplit;           // k_rowstats tiles (slices) per row
+  int64_t split_len;        // elements per slice: one tile, or less for small problems
+  int32_t nsplit_r;         // k_resid workgroups per request
   int32_t greedy_all;
   double *p_x, *q_x, *row_sum_t, *row_sum_d, *resid_mass;
   float *row_max_t, *row_max_d;
 };
 
-// ------------------------------------------------------------------ request / row helpers
+// ------------------------------------------------------------------ small helpers
 
 __device__ __forceinline__ void request(const Params &P, int32_t b, int64_t &dbase,
                                         int32_t &gb, float &T) {
@@ -106,13 +115,13 @@ __device__ __forceinline__ void request(const Params &P, int32_t b, int64_t &dba
 }
 
 struct TempConst {
-  double c;  // c_hi + c_lo exactly
+  double c;  // c_hi + c_lo exactly: log2(e)/T to ~1e-16
   float c_hi, c_lo;
 };
 
 __device__ __forceinline__ TempConst temp_const(float T) {
   double c = kLog2e / (double)T;
-  if (c > 1e38) c = 1e38;
+  if (c > 1e38) c = 1e38;  // temperatures below ~1.4e-38 act as ~1.4e-38
   const float hi = (float)c;
   const float lo = (float)(c - (double)hi);
   return {(double)hi + (double)lo, hi, lo};
@@ -128,47 +137,117 @@ __device__ __forceinline__ float logit_at(const void *base, int64_t idx) {
   }
 }
 
-// One load unit: 16 bytes (4 fp32 / 8 bf16) when rows are 16-byte aligned, else 1 element.
-template <int DT, bool VEC>
-struct Unit {
-  static constexpr int W = VEC ? (DT == SPEC_F32 ? 4 : 8) : 1;
-  __device__ static __forceinline__ void load(const void *row, int64_t u, float (&x)[W]) {
-    if constexpr (VEC) {
-      const uint4 v = static_cast<const uint4 *>(row)[u];
-      if constexpr (DT == SPEC_F32) {
-        x[0] = __uint_as_float(v.x);
-        x[1] = __uint_as_float(v.y);
-        x[2] = __uint_as_float(v.z);
-        x[3] = __uint_as_float(v.w);
-      } else {
-        x[0] = __uint_as_float(v.x << 16);
-        x[1] = __uint_as_float(v.x & 0xffff0000u);
-        x[2] = __uint_as_float(v.y << 16);
-        x[3] = __uint_as_float(v.y & 0xffff0000u);
-        x[4] = __uint_as_float(v.z << 16);
-        x[5] = __uint_as_float(v.z & 0xffff0000u);
-        x[6] = __uint_as_float(v.w << 16);
-        x[7] = __uint_as_float(v.w & 0xffff0000u);
-      }
-    } else {
-      x[0] = logit_at<DT>(row, u);
-    }
-  }
-};
-
 template <int DT>
 __device__ __forceinline__ const void *row_ptr(const void *base, int64_t row, int64_t V) {
   constexpr int64_t es = DT == SPEC_F32 ? 4 : 2;
   return static_cast<const char *>(base) + row * V * es;
 }
 
-// 2^((z - m) c) in fp32 with the exact difference and the split constant.
-__device__ __forceinline__ float exp_term(float z, float m, float c_hi, float c_lo) {
+// Load units.  VEC: rows are 16-byte aligned and a unit is one 16-byte load (4 fp32 or
+// 8 bf16); otherwise a unit is one element.
+template <int DT, bool VEC>
+struct Unit {
+  static constexpr int W = VEC ? (DT == SPEC_F32 ? 4 : 8) : 1;
+  using Raw = typename std::conditional<VEC, u32x4, float>::type;   // one unit in registers
+  using Store = typename std::conditional<                            // one unit in memory
+      VEC, u32x4, typename std::conditional<DT == SPEC_F32, float, uint16_t>::type>::type;
+
+  template <bool NT>
+  __device__ static __forceinline__ Raw load(const Store *base, int64_t u) {
+    if constexpr (VEC) {
+      if constexpr (NT) return __builtin_nontemporal_load(base + u);
+      else return base[u];
+    } else if constexpr (DT == SPEC_F32) {
+      return base[u];
+    } else {
+      return __uint_as_float((uint32_t)base[u] << 16);
+    }
+  }
+  // Filler for units past the row end: the most negative finite value (both bf16 halves;
+  // a word read as fp32 must not be a NaN for max_raw below).
+  __device__ static __forceinline__ Raw filler() {
+    if constexpr (VEC) {
+      const uint32_t v = DT == SPEC_F32 ? 0xff7fffffu : 0xff7fff7fu;
+      return u32x4{v, v, v, v};
+    } else {
+      return DT == SPEC_F32 ? -3.40282347e38f : __uint_as_float(0xff7f0000u);
+    }
+  }
+  // Running maximum over a unit without unpacking bf16 high halves.  A 32-bit word read as
+  // fp32 sorts between its high bf16 value (inclusive) and the next bf16 value away from
+  // zero (exclusive), so its order against every other bf16 value is kept, and clearing the
+  // low 16 bits of the maximum (exact_max) gives the exact maximum.
+  __device__ static __forceinline__ float max_raw(const Raw &r, float m) {
+    if constexpr (!VEC) {
+      return fmaxf(m, r);
+    } else if constexpr (DT == SPEC_F32) {
+      return fmaxf(fmaxf(m, __uint_as_float(r.x)),
+                   fmaxf(fmaxf(__uint_as_float(r.y), __uint_as_float(r.z)), __uint_as_float(r.w)));
+    } else {
+      m = fmaxf(m, fmaxf(__uint_as_float(r.x << 16), __uint_as_float(r.x)));
+      m = fmaxf(m, fmaxf(__uint_as_float(r.y << 16), __uint_as_float(r.y)));
+      m = fmaxf(m, fmaxf(__uint_as_float(r.z << 16), __uint_as_float(r.z)));
+      m = fmaxf(m, fmaxf(__uint_as_float(r.w << 16), __uint_as_float(r.w)));
+      return m;
+    }
+  }
+  __device__ static __forceinline__ float exact_max(float m) {
+    if constexpr (VEC && DT == SPEC_BF16) return __uint_as_float(__float_as_uint(m) & 0xffff0000u);
+    else return m;
+  }
+  __device__ static __forceinline__ void cvt(const Raw &r, float (&x)[W]) {
+    if constexpr (!VEC) {
+      x[0] = r;
+    } else if constexpr (DT == SPEC_F32) {
+      x[0] = __uint_as_float(r.x);
+      x[1] = __uint_as_float(r.y);
+      x[2] = __uint_as_float(r.z);
+      x[3] = __uint_as_float(r.w);
+    } else {
+      x[0] = __uint_as_float(r.x << 16);
+      x[1] = __uint_as_float(r.x & 0xffff0000u);
+      x[2] = __uint_as_float(r.y << 16);
+      x[3] = __uint_as_float(r.y & 0xffff0000u);
+      x[4] = __uint_as_float(r.z << 16);
+      x[5] = __uint_as_float(r.z & 0xffff0000u);
+      x[6] = __uint_as_float(r.w << 16);
+      x[7] = __uint_as_float(r.w & 0xffff0000u);
+    }
+  }
+};
+
+// Exponent arguments of the terms 2^(z c - shift):
+//  shifted: shift = m c exactly, computed as (z - m) c_hi + (z - m) c_lo with the exact
+//           difference first; safe for any m and c.
+//  folded:  shift = K = fp32(m c), computed as (z c_hi - K) + z c_lo: two FMAs.  The inner
+//           FMA rounds only the small difference, and z c_lo is added to it last, so no part
+//           of c is lost.  Used when |m| c < 2^22: then |m c - K| < 1/2, no term overflows.
+// Sums in either form are brought to the shifted form (shift m c) exactly in fp64.
+__device__ __forceinline__ float arg_shifted(float z, float m, float c_hi, float c_lo) {
   const float d = z - m;
-  return __builtin_amdgcn_exp2f(fmaf(d, c_hi, d * c_lo));
+  return fmaf(d, c_hi, d * c_lo);
+}
+__device__ __forceinline__ float arg_folded(float z, float K, float c_hi, float c_lo) {
+  return fmaf(z, c_lo, fmaf(z, c_hi, -K));
+}
+__device__ __forceinline__ bool fold_ok(float m, float c_hi) {
+  return fabsf(m) * c_hi < 4194304.f;
+}
+__device__ __forceinline__ float ex2(float a) { return __builtin_amdgcn_exp2f(a); }
+
+// Pairwise sum of a unit's terms (fixed order, shared by every pass that recomputes it).
+template <int W>
+__device__ __forceinline__ float unit_sum(const float (&e)[W]) {
+  if constexpr (W == 8) {
+    return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+  } else if constexpr (W == 4) {
+    return (e[0] + e[1]) + (e[2] + e[3]);
+  } else {
+    return e[0];
+  }
 }
 
-// ------------------------------------------------------------------ block reductions
+// ------------------------------------------------------------------ wave / block reductions
 
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -178,67 +257,77 @@ __device__ __forceinline__ double wave_sum(double v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
-
-__device__ float block_max(float v, float *sh) {
-  v = wave_max(v);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) sh[w] = v;
-  __syncthreads();
-  float r = sh[0];
-  for (int i = 1; i < kWaves; ++i) r = fmaxf(r, sh[i]);
-  __syncthreads();
-  return r;
+__device__ __forceinline__ int32_t wave_min_i(int32_t v) {
+  for (int o = 32; o > 0; o >>= 1) {
+    const int32_t t = __shfl_xor(v, o);
+    v = t < v ? t : v;
+  }
+  return v;
 }
-
-__device__ double block_sum(double v, double *sh) {
-  v = wave_sum(v);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) sh[w] = v;
-  __syncthreads();
-  double r = 0.0;
-  for (int i = 0; i < kWaves; ++i) r += sh[i];
-  __syncthreads();
-  return r;
-}
-
-// (max value, lowest index) lexicographic reduction.
 __device__ __forceinline__ void argmax_merge(float &bv, int32_t &bi, float ov, int32_t oi) {
   if (ov > bv || (ov == bv && oi < bi)) {
     bv = ov;
     bi = oi;
   }
 }
-
-__device__ void block_argmax(float &bv, int32_t &bi, float *shv, int32_t *shi) {
+__device__ __forceinline__ void wave_argmax(float &bv, int32_t &bi) {
   for (int o = 32; o > 0; o >>= 1) {
     const float ov = __shfl_xor(bv, o);
     const int32_t oi = __shfl_xor(bi, o);
     argmax_merge(bv, bi, ov, oi);
   }
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    shv[w] = bv;
-    shi[w] = bi;
+}
+
+// Inclusive scan over a wavefront (fp64, lane order).
+__device__ __forceinline__ double wave_incl_scan(double v) {
+  const int lane = threadIdx.x & 63;
+  for (int o = 1; o < 64; o <<= 1) {
+    const double t = __shfl_up(v, o);
+    if (lane >= o) v += t;
   }
+  return v;
+}
+
+// Block reductions with one barrier each.  Every call site owns its LDS array, and the next
+// write to that array is separated from these reads by another reduction's barrier.
+__device__ __forceinline__ float block_max1(float v, float *sh) {
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
   __syncthreads();
-  bv = shv[0];
-  bi = shi[0];
-  for (int i = 1; i < kWaves; ++i) argmax_merge(bv, bi, shv[i], shi[i]);
+  float r = sh[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) r = fmaxf(r, sh[i]);
+  return r;
+}
+__device__ __forceinline__ double block_sum1(double v, double *sh) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
   __syncthreads();
+  double r = sh[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) r += sh[i];
+  return r;
+}
+__device__ __forceinline__ int32_t block_min1(int32_t v, int32_t *sh) {
+  v = wave_min_i(v);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int32_t r = sh[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) r = sh[i] < r ? sh[i] : r;
+  return r;
 }
 
 // Exclusive scan over the block in thread order (fp64); also returns the block total.
-__device__ double block_exclusive_scan(double v, double *sh, double &total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  double inc = v;
-  for (int o = 1; o < 64; o <<= 1) {
-    const double t = __shfl_up(inc, o);
-    if (lane >= o) inc += t;
-  }
-  if (lane == 63) sh[w] = inc;
+// Ends with a barrier so `sh` can be reused at once.
+__device__ double block_excl_scan(double v, double *sh, double &total) {
+  const int w = threadIdx.x >> 6;
+  const double inc = wave_incl_scan(v);
+  if ((threadIdx.x & 63) == 63) sh[w] = inc;
   __syncthreads();
   double off = 0.0;
   total = 0.0;
+#pragma unroll
   for (int i = 0; i < kWaves; ++i) {
     if (i < w) off += sh[i];
     total += sh[i];
@@ -247,27 +336,58 @@ __device__ double block_exclusive_scan(double v, double *sh, double &total) {
   return off + inc - v;
 }
 
-// ------------------------------------------------------------------ 1. row statistics
+// First / last thread (by id) for which `pred` holds, block-wide: INT32_MAX / -1 if none.
+__device__ int32_t block_first(bool pred, int32_t *sh) {
+  const uint64_t m = __ballot(pred);
+  if ((threadIdx.x & 63) == 0)
+    sh[threadIdx.x >> 6] = m ? (int32_t)(threadIdx.x & ~63u) + __ffsll((long long)m) - 1 : INT32_MAX;
+  __syncthreads();
+  int32_t r = INT32_MAX;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) r = sh[i] < r ? sh[i] : r;
+  __syncthreads();
+  return r;
+}
+__device__ int32_t block_last(bool pred, int32_t *sh) {
+  const uint64_t m = __ballot(pred);
+  if ((threadIdx.x & 63) == 0)
+    sh[threadIdx.x >> 6] = m ? (int32_t)(threadIdx.x & ~63u) + 63 - __clzll((long long)m) : -1;
+  __syncthreads();
+  int32_t r = -1;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) r = sh[i] > r ? sh[i] : r;
+  __syncthreads();
+  return r;
+}
 
+// ------------------------------------------------------------------ k_rowstats
+
+struct StatsLds {
+  float mx[kWaves];
+  double sum[kWaves];
+  int32_t idx[kWaves];
+};
+
+// One workgroup per (row slot, tile): blockIdx.x is the tile of the row, blockIdx.y +
+// blockIdx.z * gridDim.y the row slot (request * spr + slot).  Slots beyond a request's rows
+// (gamma_b < gamma, or draft rows of a greedy request) exit at once.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_rowstats(Params P) {
   using U = Unit<DT, VEC>;
+  using Store = typename U::Store;
   constexpr int W = U::W;
-  __shared__ float shf[kWaves];
-  __shared__ double shd[kWaves];
-  __shared__ int32_t shi[kWaves];
-
-  const int64_t wg = blockIdx.x;
-  const int32_t split = (int32_t)(wg % P.nsplit);
-  const int64_t slot = wg / P.nsplit;
-  const int32_t b = (int32_t)(slot / P.spr);
-  const int32_t k = (int32_t)(slot % P.spr);
+  constexpr int NV = int(kTileElems / kThreads) / W;  // units per thread
+  __shared__ StatsLds sh;
+  const int tid = threadIdx.x;
+  const uint32_t slot = blockIdx.y + blockIdx.z * gridDim.y;
+  const uint32_t spr = (uint32_t)P.spr;
+  if (slot >= (uint32_t)P.B * spr) return;
+  const int32_t b = (int32_t)(slot / spr);
+  const int32_t k = (int32_t)(slot - (uint32_t)b * spr);
   int64_t dbase;
   int32_t gb;
   float T;
   request(P, b, dbase, gb, T);
-  const bool sampling = T > 0.f;
-
   const void *base;
   int64_t row;
   if (k <= P.gamma) {
@@ -276,355 +396,366 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Params P) {
     row = dbase + b + k;
   } else {
     const int32_t i = k - P.gamma - 1;
-    if (i >= gb || !sampling) return;
+    if (i >= gb || !(T > 0.f)) return;
     base = P.draft;
     row = dbase + i;
   }
-  const void *rp = row_ptr<DT>(base, row, P.V);
-  const int64_t lo = (int64_t)split * P.split_len;
+  const int64_t lo = (int64_t)blockIdx.x * P.split_len;
   const int64_t hi = lo + P.split_len < P.V ? lo + P.split_len : P.V;
-  const int64_t u0 = lo / W, u1 = hi > lo ? hi / W : u0;  // lo, hi are multiples of W
-  Partial *out = P.parts + slot * P.nsplit + split;
-  const int tid = threadIdx.x;
+  const Store *tile = static_cast<const Store *>(row_ptr<DT>(base, row, P.V)) + lo / W;
+  const int32_t nu = (int32_t)((hi - lo + W - 1) / W);
 
-  if (sampling) {
+  // The tile's loads go out before anything else; units past the row end hold the filler.
+  typename U::Raw raw[NV];
+  if (nu == kThreads * NV) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) raw[j] = U::template load<true>(tile, j * kThreads + tid);
+  } else {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int32_t u = j * kThreads + tid;
+      raw[j] = u < nu ? U::template load<true>(tile, u) : U::filler();
+    }
+  }
+  float tm = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) tm = U::max_raw(raw[j], tm);
+  const float M = U::exact_max(block_max1(tm, sh.mx));
+  Partial *out = P.parts + (int64_t)slot * P.nsplit + blockIdx.x;
+
+  if (T > 0.f) {
     const TempConst tc = temp_const(T);
-    float m = -INFINITY;
-    double s = 0.0;
-    for (int64_t ub = u0; ub < u1; ub += (int64_t)kThreads * kUnroll) {
-      if (ub + tid >= u1) break;
-      float x[kUnroll][W];
-      bool ok[kUnroll];
+    double acc = 0.0;
+    if (fold_ok(M, tc.c_hi) && tc.c < 1e6 && tc.c > 1e-30) {
+      // The common case: two-FMA exponent arguments.  In this range of c a filler's
+      // argument is -inf or below -200, so its term is exactly 0 and needs no mask.
+      const float K = (float)((double)M * tc.c);
 #pragma unroll
-      for (int j = 0; j < kUnroll; ++j) {
-        const int64_t u = ub + (int64_t)j * kThreads + tid;
-        ok[j] = u < u1;
-        if (ok[j]) {
-          U::load(rp, u, x[j]);
-        } else {
+      for (int j = 0; j < NV; ++j) {
+        float x[W], e[W];
+        U::cvt(raw[j], x);
 #pragma unroll
-          for (int e = 0; e < W; ++e) x[j][e] = -INFINITY;
+        for (int q = 0; q < W; ++q) e[q] = ex2(arg_folded(x[q], K, tc.c_hi, tc.c_lo));
+        acc += (double)unit_sum<W>(e);
+      }
+      const double S = block_sum1(acc, sh.sum);
+      // to the shifted form, sum 2^((z - M) c): factor 2^(K - M c), one rounding
+      if (tid == 0) *out = Partial{M, 0, S * exp2(fma(-(double)M, tc.c, (double)K))};
+    } else {
+      // Extreme temperatures or logits: overflow-safe arguments, units re-read one at a time
+      // (cache hits) to keep this rare path out of the common path's registers.
+#pragma unroll 1
+      for (int j = 0; j < NV; ++j) {
+        const int32_t u = j * kThreads + tid;
+        if (u < nu) {
+          float x[W], e[W];
+          U::cvt(U::template load<false>(tile, u), x);
+#pragma unroll
+          for (int q = 0; q < W; ++q) e[q] = ex2(arg_shifted(x[q], M, tc.c_hi, tc.c_lo));
+          acc += (double)unit_sum<W>(e);
         }
       }
-      float cm = m;
-#pragma unroll
-      for (int j = 0; j < kUnroll; ++j)
-#pragma unroll
-        for (int e = 0; e < W; ++e) cm = fmaxf(cm, x[j][e]);
-      if (cm > m) {
-        s *= exp2(((double)m - (double)cm) * tc.c);
-        m = cm;
-      }
-#pragma unroll
-      for (int j = 0; j < kUnroll; ++j) {
-#pragma unroll
-        for (int e = 0; e < W; ++e) {
-          const float t = exp_term(x[j][e], m, tc.c_hi, tc.c_lo);
-          s += ok[j] ? (double)t : 0.0;
-        }
-      }
-    }
-    const float M = block_max(m, shf);
-    const double scaled = (m == -INFINITY) ? 0.0 : s * exp2(((double)m - (double)M) * tc.c);
-    const double S = block_sum(scaled, shd);
-    if (tid == 0) {
-      out->m = M;
-      out->idx = 0;
-      out->s = S;
+      const double S = block_sum1(acc, sh.sum);
+      if (tid == 0) *out = Partial{M, 0, S};
     }
   } else {
-    float bv = -INFINITY;
-    int32_t bi = INT32_MAX;
-    for (int64_t ub = u0; ub < u1; ub += (int64_t)kThreads * kUnroll) {
-      if (ub + tid >= u1) break;
+    // Greedy row: the lowest index holding the tile maximum.
+    int32_t ti = INT32_MAX;
 #pragma unroll
-      for (int j = 0; j < kUnroll; ++j) {
-        const int64_t u = ub + (int64_t)j * kThreads + tid;
-        if (u < u1) {
-          float x[W];
-          U::load(rp, u, x);
+    for (int j = 0; j < NV; ++j) {
+      float x[W];
+      U::cvt(raw[j], x);
+      const int32_t u = j * kThreads + tid;
 #pragma unroll
-          for (int e = 0; e < W; ++e) {
-            if (x[e] > bv) {
-              bv = x[e];
-              bi = (int32_t)(u * W + e);
-            }
-          }
-        }
-      }
+      for (int q = 0; q < W; ++q)
+        if (ti == INT32_MAX && u < nu && x[q] == M) ti = (int32_t)((lo / W + u) * W + q);
     }
-    block_argmax(bv, bi, shf, shi);
-    if (tid == 0) {
-      out->m = bv;
-      out->idx = bi;
-      out->s = 0.0;
-    }
+    const int32_t bi = block_min1(ti, sh.idx);
+    if (tid == 0) *out = Partial{M, bi, 0.0};
   }
 }
 
-// ------------------------------------------------------------------ 2. decide
+// ------------------------------------------------------------------ k_resid
 
-__device__ void merge_stats(const Params &P, int64_t slot, double c, double &m, double &s) {
-  const Partial *pp = P.parts + slot * P.nsplit;
-  float mx = -INFINITY;
-  for (int i = 0; i < P.nsplit; ++i) mx = fmaxf(mx, pp[i].m);
-  double acc = 0.0;
-  for (int i = 0; i < P.nsplit; ++i) {
-    const Partial q = pp[i];
-    if (q.m != -INFINITY) acc += q.s * exp2(((double)q.m - (double)mx) * c);
-  }
-  m = mx;
-  s = acc;
-}
-
-__device__ void merge_argmax(const Params &P, int64_t slot, float &bv, int32_t &bi) {
-  const Partial *pp = P.parts + slot * P.nsplit;
-  bv = -INFINITY;
-  bi = INT32_MAX;
-  for (int i = 0; i < P.nsplit; ++i) argmax_merge(bv, bi, pp[i].m, pp[i].idx);
-}
-
-template <int DT>
-__global__ __launch_bounds__(kThreads) void k_decide(Params P) {
-  const int lane = threadIdx.x & 63;
-  const int32_t b = (int32_t)(blockIdx.x * kWaves + (threadIdx.x >> 6));
-  if (b >= P.B) return;
-  int64_t dbase;
-  int32_t gb;
-  float T;
-  request(P, b, dbase, gb, T);
-  const int64_t tbase = dbase + b;
-  const bool sampling = T > 0.f;
-  const int64_t slot0 = (int64_t)b * P.spr;
-  const int64_t dslot0 = slot0 + P.gamma + 1;
-  const TempConst tc = temp_const(sampling ? T : 1.f);
-
-  bool accept = false;
-  if (lane < gb) {
-    const int32_t x = P.tokens[dbase + lane];
-    if (!sampling) {
-      float bv;
-      int32_t bi;
-      merge_argmax(P, slot0 + lane, bv, bi);
-      accept = x == bi;
+// Residual weight of one element of the stop row, scaled by S_t:
+//   residual mode: S_t (p_k - q_k)_+ = (e_t - rho e_d)_+ with rho = S_t / S_d (two-float);
+//   bonus mode:    S_t p_k = e_t.
+template <int W>
+__device__ __forceinline__ void resid_weights(const float (&zt)[W], const float (&zd)[W],
+                                              const Stop &st, float (&r)[W]) {
+#pragma unroll
+  for (int q = 0; q < W; ++q) {
+    const float et = ex2(arg_shifted(zt[q], st.mt, st.c_hi, st.c_lo));
+    if (st.mode == kModeResidual) {
+      const float ed = ex2(arg_shifted(zd[q], st.md, st.c_hi, st.c_lo));
+      const float v = fmaf(-ed, st.rho_lo, fmaf(-ed, st.rho_hi, et));
+      r[q] = v > 0.f ? v : 0.f;
     } else {
-      double mt, st, md, sd;
-      merge_stats(P, slot0 + lane, tc.c, mt, st);
-      merge_stats(P, dslot0 + lane, tc.c, md, sd);
-      double p = 0.0, q = 0.0;
-      if (x >= 0 && x < P.V) {
-        const double zt = logit_at<DT>(P.target, (tbase + lane) * P.V + x);
-        const double zd = logit_at<DT>(P.draft, (dbase + lane) * P.V + x);
-        p = exp2((zt - mt) * tc.c) / st;
-        q = exp2((zd - md) * tc.c) / sd;
-      }
-      const double u = (double)P.uniforms[2 * (tbase + lane)];
-      accept = u * q < p;
-      if (P.p_x) P.p_x[dbase + lane] = p;
-      if (P.q_x) P.q_x[dbase + lane] = q;
+      r[q] = et;
     }
   }
-  const uint64_t acc_mask = __ballot(accept);
-  const uint64_t valid = gb >= 64 ? ~0ull : ((1ull << gb) - 1ull);
-  const uint64_t rej = ~acc_mask & valid;
-  const int32_t j = rej ? (int32_t)(__ffsll((long long)rej) - 1) : gb;
-
-  for (int32_t i = lane; i <= gb; i += 64) {
-    if (i != j) P.out_tokens[tbase + i] = i < j ? P.tokens[dbase + i] : -1;
-  }
-  if (lane == 0) {
-    P.out_n[b] = j;
-    Stop st = {};
-    st.j = j;
-    if (!sampling) {
-      float bv;
-      int32_t bi;
-      merge_argmax(P, slot0 + j, bv, bi);
-      P.out_tokens[tbase + j] = bi;
-      st.mode = kModeNone;
-    } else {
-      double mt, s_t;
-      merge_stats(P, slot0 + j, tc.c, mt, s_t);
-      st.mt = (float)mt;
-      st.st = s_t;
-      st.c = tc.c;
-      st.c_hi = tc.c_hi;
-      st.c_lo = tc.c_lo;
-      if (j < gb) {
-        double md, s_d;
-        merge_stats(P, dslot0 + j, tc.c, md, s_d);
-        st.md = (float)md;
-        st.sd = s_d;
-        st.k = (mt - md) * tc.c + log2(s_t / s_d);
-        st.mode = kModeResidual;
-      } else {
-        st.mode = kModeBonus;
-      }
-    }
-    P.stop[b] = st;
-  }
-
-  // Diagnostics.
-  if (P.row_max_t || P.row_sum_t) {
-    for (int32_t i = lane; i <= gb; i += 64) {
-      if (sampling) {
-        double m, s;
-        merge_stats(P, slot0 + i, tc.c, m, s);
-        if (P.row_max_t) P.row_max_t[tbase + i] = (float)m;
-        if (P.row_sum_t) P.row_sum_t[tbase + i] = s;
-      } else if (P.row_max_t) {
-        float bv;
-        int32_t bi;
-        merge_argmax(P, slot0 + i, bv, bi);
-        P.row_max_t[tbase + i] = bv;
-      }
-    }
-  }
-  if (sampling && (P.row_max_d || P.row_sum_d)) {
-    for (int32_t i = lane; i < gb; i += 64) {
-      double m, s;
-      merge_stats(P, dslot0 + i, tc.c, m, s);
-      if (P.row_max_d) P.row_max_d[dbase + i] = (float)m;
-      if (P.row_sum_d) P.row_sum_d[dbase + i] = s;
-    }
-  }
-}
-
-// ------------------------------------------------------------------ 3. residual mass
-
-// Unnormalised weight of token k at the stop row: S_t * max(p_k - q_k, 0), or S_t * p_k.
-template <int MODE>
-__device__ __forceinline__ float resid_weight(float zt, float zd, const Stop &st) {
-  const float et = exp_term(zt, st.mt, st.c_hi, st.c_lo);
-  if constexpr (MODE == kModeBonus) {
-    return et;
-  } else {
-    const double delta = ((double)zd - (double)zt) * st.c + st.k;  // log2(q_k / p_k)
-    if (!(delta < 0.0)) return 0.f;
-    return et * -expm1f((float)(delta * kLn2));
-  }
-}
-
-template <int DT, bool VEC, int MODE>
-__device__ double resid_range_sum(const void *tr, const void *dr, int64_t u0, int64_t u1,
-                                  const Stop &st) {
-  using U = Unit<DT, VEC>;
-  constexpr int W = U::W;
-  double acc = 0.0;
-  for (int64_t u = u0 + threadIdx.x; u < u1; u += kThreads) {
-    float zt[W], zd[W];
-    U::load(tr, u, zt);
-    if constexpr (MODE == kModeResidual) U::load(dr, u, zd);
-#pragma unroll
-    for (int e = 0; e < W; ++e)
-      acc += (double)resid_weight<MODE>(zt[e], MODE == kModeResidual ? zd[e] : 0.f, st);
-  }
-  return acc;
 }
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_resid(Params P) {
-  constexpr int W = Unit<DT, VEC>::W;
-  __shared__ double shd[kWaves];
-  const int64_t wg = blockIdx.x;
-  const int32_t b = (int32_t)(wg / P.nsplit_r);
-  const int32_t split = (int32_t)(wg % P.nsplit_r);
-  const Stop st = P.stop[b];
-  if (st.mode == kModeNone) return;
+  using U = Unit<DT, VEC>;
+  using Store = typename U::Store;
+  constexpr int W = U::W;
+  constexpr int NC = kResChunksInFlight;
+  constexpr int kRows = 2 * SPEC_MAX_GAMMA + 1;
+  __shared__ float s_m[kRows];
+  __shared__ double s_s[kRows];
+  __shared__ int32_t s_i[SPEC_MAX_GAMMA + 1];
+  __shared__ int32_t s_j;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t b = (int32_t)(blockIdx.x / P.nsplit_r);
+  const int32_t split = (int32_t)(blockIdx.x % P.nsplit_r);
   int64_t dbase;
   int32_t gb;
   float T;
   request(P, b, dbase, gb, T);
-  const void *tr = row_ptr<DT>(P.target, dbase + b + st.j, P.V);
-  const void *dr = row_ptr<DT>(P.draft, dbase + st.j, P.V);
-  const int64_t lo = (int64_t)split * P.split_len_r;
-  const int64_t hi = lo + P.split_len_r < P.V ? lo + P.split_len_r : P.V;
-  const int64_t u0 = lo / W, u1 = hi > lo ? hi / W : u0;
-  double acc = st.mode == kModeResidual
-                   ? resid_range_sum<DT, VEC, kModeResidual>(tr, dr, u0, u1, st)
-                   : resid_range_sum<DT, VEC, kModeBonus>(tr, dr, u0, u1, st);
-  acc = block_sum(acc, shd);
-  if (threadIdx.x == 0) P.rsum[(int64_t)b * P.nsplit_r + split] = acc;
-}
+  const bool sampling = T > 0.f;
+  if (!sampling && split != 0) return;  // one workgroup finishes a greedy request
+  const int64_t tbase = dbase + b;
+  const int32_t ntr = gb + 1;
+  const int32_t nrows = ntr + (sampling ? gb : 0);
+  const int64_t slot0 = (int64_t)b * P.spr;
+  const TempConst tc = temp_const(sampling ? T : 1.f);
 
-// ------------------------------------------------------------------ 4. draw
-
-// Inverse CDF inside units [u0, u1) of the stop row: each thread owns a contiguous run of
-// units; a block scan of the run totals picks the thread, which then walks its run.
-// If `frac` is set, the target is u * (total of the range); otherwise it is `target`.
-template <int DT, bool VEC, int MODE>
-__device__ int32_t draw_in_range(const void *tr, const void *dr, int64_t u0, int64_t u1,
-                                 const Stop &st, double target, bool frac, double u,
-                                 double &range_total) {
-  using U = Unit<DT, VEC>;
-  constexpr int W = U::W;
-  __shared__ double shs[kWaves];
-  __shared__ int32_t sh_first[kWaves], sh_last[kWaves];
-  const int tid = threadIdx.x;
-  const int64_t n = u1 - u0;
-  const int64_t per = (n + kThreads - 1) / kThreads;
-  const int64_t a = u0 + tid * per;
-  const int64_t e_ = a + per < u1 ? a + per : u1;
-
-  double mine = 0.0;
-  for (int64_t uu = a; uu < e_; ++uu) {
-    float zt[W], zd[W];
-    U::load(tr, uu, zt);
-    if constexpr (MODE == kModeResidual) U::load(dr, uu, zd);
+  // 1. Merge row partials: wavefront w takes rows w, w+4, ...; lane p holds slice p.
+  for (int32_t r0 = 0; r0 < nrows; r0 += kWaves * 4) {
+    Partial pv[4];
 #pragma unroll
-    for (int e = 0; e < W; ++e)
-      mine += (double)resid_weight<MODE>(zt[e], MODE == kModeResidual ? zd[e] : 0.f, st);
-  }
-  double total;
-  const double before = block_exclusive_scan(mine, shs, total);
-  range_total = total;
-  if (frac) target = u * total;
-
-  // first thread whose run crosses the target; last thread with positive mass
-  const bool crosses = mine > 0.0 && before + mine > target;
-  const uint64_t cm = __ballot(crosses), pm = __ballot(mine > 0.0);
-  const int w = tid >> 6;
-  if ((tid & 63) == 0) {
-    sh_first[w] = cm ? w * 64 + __ffsll((long long)cm) - 1 : INT32_MAX;
-    sh_last[w] = pm ? w * 64 + 63 - __clzll((long long)pm) : -1;
-  }
-  __syncthreads();
-  int32_t first = INT32_MAX, last = -1;
-  for (int i = 0; i < kWaves; ++i) {
-    first = sh_first[i] < first ? sh_first[i] : first;
-    last = sh_last[i] > last ? sh_last[i] : last;
-  }
-  __syncthreads();
-  const int32_t pick = first != INT32_MAX ? first : last;
-  const bool exact = first != INT32_MAX;
-  int32_t result = -1;
-  if (pick >= 0 && tid == pick) {
-    double run = before;
-    int32_t last_pos = -1;
-    for (int64_t uu = a; uu < e_ && result < 0; ++uu) {
-      float zt[W], zd[W];
-      U::load(tr, uu, zt);
-      if constexpr (MODE == kModeResidual) U::load(dr, uu, zd);
+    for (int q = 0; q < 4; ++q) {
+      const int32_t r = r0 + wave + kWaves * q;
+      pv[q].m = -INFINITY;
+      pv[q].idx = INT32_MAX;
+      pv[q].s = 0.0;
+      if (r < nrows && lane < P.nsplit) {
+        const int64_t slot = r < ntr ? slot0 + r : slot0 + P.gamma + 1 + (r - ntr);
+        pv[q] = P.parts[slot * P.nsplit + lane];
+      }
+    }
 #pragma unroll
-      for (int e = 0; e < W; ++e) {
-        const float r = resid_weight<MODE>(zt[e], MODE == kModeResidual ? zd[e] : 0.f, st);
-        run += (double)r;
-        if (r > 0.f) {
-          last_pos = (int32_t)(uu * W + e);
-          if (exact && result < 0 && run > target) result = last_pos;
+    for (int q = 0; q < 4; ++q) {
+      const int32_t r = r0 + wave + kWaves * q;
+      if (r >= nrows) break;  // uniform across the wavefront
+      const Partial *rowp = P.parts + (r < ntr ? slot0 + r : slot0 + P.gamma + 1 + (r - ntr)) * P.nsplit;
+      if (sampling) {
+        float m = pv[q].m;
+        for (int32_t p = lane + 64; p < P.nsplit; p += 64) m = fmaxf(m, rowp[p].m);
+        const float M = wave_max(m);
+        double f = pv[q].m != -INFINITY
+                       ? pv[q].s * exp2(((double)pv[q].m - (double)M) * tc.c)
+                       : 0.0;
+        for (int32_t p = lane + 64; p < P.nsplit; p += 64) {
+          const Partial o = rowp[p];
+          if (o.m != -INFINITY) f += o.s * exp2(((double)o.m - (double)M) * tc.c);
+        }
+        const double S = wave_sum(f);
+        if (lane == 0) {
+          s_m[r] = M;
+          s_s[r] = S;
+        }
+      } else {
+        float bv = pv[q].m;
+        int32_t bi = pv[q].idx;
+        for (int32_t p = lane + 64; p < P.nsplit; p += 64) argmax_merge(bv, bi, rowp[p].m, rowp[p].idx);
+        wave_argmax(bv, bi);
+        if (lane == 0) {
+          s_m[r] = bv;
+          s_i[r] = bi;
         }
       }
     }
-    if (result < 0) result = last_pos;
   }
-  return result;  // valid in thread `pick` only; -1 elsewhere
+  __syncthreads();
+
+  // 2. Accept tests (lane i = draft position i) and the first rejection; slice 0 writes.
+  if (wave == 0) {
+    bool accept = false;
+    double p = 0.0, q = 0.0;
+    if (lane < gb) {
+      const int32_t x = P.tokens[dbase + lane];
+      if (!sampling) {
+        accept = x == s_i[lane];
+      } else {
+        if (x >= 0 && x < P.V) {
+          const double zt = logit_at<DT>(P.target, (tbase + lane) * P.V + x);
+          const double zd = logit_at<DT>(P.draft, (dbase + lane) * P.V + x);
+          p = exp2((zt - (double)s_m[lane]) * tc.c) / s_s[lane];
+          q = exp2((zd - (double)s_m[ntr + lane]) * tc.c) / s_s[ntr + lane];
+        }
+        const double u = (double)P.uniforms[2 * (tbase + lane)];
+        accept = u * q < p;
+      }
+    }
+    const uint64_t acc_mask = __ballot(accept);
+    const uint64_t valid = gb >= 64 ? ~0ull : ((1ull << gb) - 1ull);
+    const uint64_t rej = ~acc_mask & valid;
+    const int32_t j = rej ? (int32_t)(__ffsll((long long)rej) - 1) : gb;
+    if (lane == 0) s_j = j;
+    if (split == 0) {
+      for (int32_t i = lane; i <= gb; i += 64) {
+        if (i != j) P.out_tokens[tbase + i] = i < j ? P.tokens[dbase + i] : -1;
+      }
+      if (lane == 0) {
+        P.out_n[b] = j;
+        Stop st = {};
+        st.j = j;
+        if (!sampling) {
+          P.out_tokens[tbase + j] = s_i[j];
+          st.mode = kModeNone;
+        } else {
+          st.mode = j < gb ? kModeResidual : kModeBonus;
+          st.mt = s_m[j];
+          st.st = s_s[j];
+          st.c_hi = tc.c_hi;
+          st.c_lo = tc.c_lo;
+          if (j < gb) {
+            st.md = s_m[ntr + j];
+            const double rho = s_s[j] / s_s[ntr + j];
+            st.rho_hi = (float)rho;
+            st.rho_lo = (float)(rho - (double)st.rho_hi);
+          }
+        }
+        P.stop[b] = st;
+      }
+      if (sampling && lane < gb) {
+        if (P.p_x) P.p_x[dbase + lane] = p;
+        if (P.q_x) P.q_x[dbase + lane] = q;
+      }
+    }
+  }
+  if (split == 0) {
+    for (int32_t r = tid; r < nrows; r += kThreads) {
+      if (r < ntr) {
+        if (P.row_max_t) P.row_max_t[tbase + r] = s_m[r];
+        if (sampling && P.row_sum_t) P.row_sum_t[tbase + r] = s_s[r];
+      } else {
+        if (P.row_max_d) P.row_max_d[dbase + r - ntr] = s_m[r];
+        if (P.row_sum_d) P.row_sum_d[dbase + r - ntr] = s_s[r];
+      }
+    }
+  }
+  __syncthreads();
+  if (!sampling) return;
+
+  // 3. This slice of the stop row(s): one fp64 sum per 64-unit chunk, chunks interleaved
+  //    across the wavefronts, NC chunks in flight per wavefront.
+  const int32_t j = s_j;
+  Stop st = {};
+  st.mode = j < gb ? kModeResidual : kModeBonus;
+  st.mt = s_m[j];
+  st.c_hi = tc.c_hi;
+  st.c_lo = tc.c_lo;
+  if (j < gb) {
+    st.md = s_m[ntr + j];
+    const double rho = s_s[j] / s_s[ntr + j];
+    st.rho_hi = (float)rho;
+    st.rho_lo = (float)(rho - (double)st.rho_hi);
+  }
+  const Store *tr = static_cast<const Store *>(row_ptr<DT>(P.target, tbase + j, P.V));
+  const Store *dr = static_cast<const Store *>(row_ptr<DT>(P.draft, dbase + j, P.V));
+  const int64_t nunits = (P.V + W - 1) / W;
+  const int64_t nchunks = (nunits + 63) / 64;
+  const int64_t per = (nchunks + P.nsplit_r - 1) / P.nsplit_r;
+  const int64_t c_lo = (int64_t)split * per;
+  const int64_t c_hi = c_lo + per < nchunks ? c_lo + per : nchunks;
+  double *cs = P.chunk_sums + (int64_t)b * P.chunk_stride;
+  for (int64_t c0 = c_lo + wave; c0 < c_hi; c0 += (int64_t)kWaves * NC) {
+    typename U::Raw rt[NC], rd[NC];
+#pragma unroll
+    for (int q = 0; q < NC; ++q) {
+      const int64_t c = c0 + (int64_t)q * kWaves;
+      const int64_t u = c * 64 + lane;
+      const bool ok = c < c_hi && u < nunits;
+      rt[q] = ok ? U::template load<false>(tr, u) : U::filler();
+      rd[q] = ok && st.mode == kModeResidual ? U::template load<false>(dr, u) : U::filler();
+    }
+#pragma unroll
+    for (int q = 0; q < NC; ++q) {
+      const int64_t c = c0 + (int64_t)q * kWaves;
+      if (c >= c_hi) break;  // uniform across the wavefront
+      float zt[W], zd[W], r[W];
+      U::cvt(rt[q], zt);
+      U::cvt(rd[q], zd);
+      resid_weights<W>(zt, zd, st, r);
+      const float us = unit_sum<W>(r);
+      const double s = wave_sum(c * 64 + lane < nunits ? (double)us : 0.0);
+      if (lane == 0) cs[c] = s;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ k_draw
+
+// Weights and pairwise sum of unit u of the stop row(s).
+template <int DT, bool VEC>
+__device__ __forceinline__ float resid_unit(const typename Unit<DT, VEC>::Store *tr,
+                                            const typename Unit<DT, VEC>::Store *dr, int64_t u,
+                                            const Stop &st, float (&r)[Unit<DT, VEC>::W]) {
+  using U = Unit<DT, VEC>;
+  constexpr int W = U::W;
+  float zt[W], zd[W];
+  U::cvt(U::template load<false>(tr, u), zt);
+  if (st.mode == kModeResidual) {
+    U::cvt(U::template load<false>(dr, u), zd);
+  } else {
+#pragma unroll
+    for (int q = 0; q < W; ++q) zd[q] = 0.f;
+  }
+  resid_weights<W>(zt, zd, st, r);
+  return unit_sum<W>(r);
+}
+
+// Draw from p over a whole target row (used only when the residual is empty after rounding).
+template <int DT>
+__device__ int32_t draw_from_row(const void *tr, int64_t V, const Stop &st, double u,
+                                 double *shd, int32_t *shi, double &total) {
+  const int tid = threadIdx.x;
+  const int64_t per = (V + kThreads - 1) / kThreads;
+  const int64_t a = tid * per;
+  const int64_t e_ = a + per < V ? a + per : V;
+  double mine = 0.0;
+  for (int64_t k = a; k < e_; ++k)
+    mine += (double)ex2(arg_shifted(logit_at<DT>(tr, k), st.mt, st.c_hi, st.c_lo));
+  const double before = block_excl_scan(mine, shd, total);
+  const double target = u * total;
+  const int32_t first = block_first(mine > 0.0 && before + mine > target, shi);
+  const int32_t last = block_last(mine > 0.0, shi);
+  const int32_t pick = first != INT32_MAX ? first : last;
+  int32_t tok = -1;
+  if (tid == pick) {
+    double run = before;
+    int32_t lastpos = -1;
+    for (int64_t k = a; k < e_; ++k) {
+      const float e = ex2(arg_shifted(logit_at<DT>(tr, k), st.mt, st.c_hi, st.c_lo));
+      run += (double)e;
+      if (e > 0.f) {
+        lastpos = (int32_t)k;
+        if (first != INT32_MAX && run > target) {
+          tok = (int32_t)k;
+          break;
+        }
+      }
+    }
+    if (tok < 0) tok = lastpos;
+  }
+  return tok;
 }
 
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_sample(Params P) {
-  constexpr int W = Unit<DT, VEC>::W;
-  __shared__ double sh_target, sh_R;
-  __shared__ int32_t sh_split, sh_token;
+__global__ __launch_bounds__(kThreads) void k_draw(Params P) {
+  using U = Unit<DT, VEC>;
+  using Store = typename U::Store;
+  constexpr int W = U::W;
+  __shared__ int32_t s_c, s_tok;
+  __shared__ double s_local;
+  __shared__ double shd[kWaves];
+  __shared__ int32_t shi[kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t b = blockIdx.x;
   const Stop st = P.stop[b];
   if (st.mode == kModeNone) return;
@@ -633,64 +764,98 @@ __global__ __launch_bounds__(kThreads) void k_sample(Params P) {
   float T;
   request(P, b, dbase, gb, T);
   const int64_t tbase = dbase + b;
-  const void *tr = row_ptr<DT>(P.target, tbase + st.j, P.V);
-  const void *dr = row_ptr<DT>(P.draft, dbase + st.j, P.V);
-  const double u = (double)P.uniforms[2 * (tbase + st.j) + 1];
-  const double *rs = P.rsum + (int64_t)b * P.nsplit_r;
+  const int32_t j = st.j;
+  const Store *tr = static_cast<const Store *>(row_ptr<DT>(P.target, tbase + j, P.V));
+  const Store *dr = static_cast<const Store *>(row_ptr<DT>(P.draft, dbase + j, P.V));
+  const double u = (double)P.uniforms[2 * (tbase + j) + 1];
+  const int64_t nunits = (P.V + W - 1) / W;
+  const int64_t nchunks = (nunits + 63) / 64;
+  const double *cs = P.chunk_sums + (int64_t)b * P.chunk_stride;
 
-  if (threadIdx.x == 0) {
-    double R = 0.0;
-    for (int s = 0; s < P.nsplit_r; ++s) R += rs[s];
-    const double target = u * R;
-    double C = 0.0;
-    int32_t pick = -1, last = -1;
-    double local = 0.0;
-    for (int s = 0; s < P.nsplit_r; ++s) {
-      const double r = rs[s];
-      if (r > 0.0) {
-        last = s;
-        if (C + r > target) {
-          pick = s;
-          local = target - C;
+  // Chunk holding u * R: each thread sums a contiguous run of chunks, a block scan places
+  // the runs, and the thread whose run crosses the target walks it.
+  const int64_t per = (nchunks + kThreads - 1) / kThreads;
+  const int64_t a = tid * per;
+  const int64_t e_ = a + per < nchunks ? a + per : nchunks;
+  double mine = 0.0;
+  for (int64_t c = a; c < e_; ++c) mine += cs[c];
+  double R;
+  const double before = block_excl_scan(mine, shd, R);
+  const double target = u * R;
+  const int32_t first = block_first(mine > 0.0 && before + mine > target, shi);
+  const int32_t lastt = block_last(mine > 0.0, shi);
+  if (tid == 0) {
+    s_c = -1;
+    s_tok = -1;
+  }
+  __syncthreads();
+  const int32_t pick = first != INT32_MAX ? first : lastt;
+  if (tid == pick) {
+    double run = before;
+    int64_t lastpos = -1;
+    for (int64_t c = a; c < e_; ++c) {
+      const double v = cs[c];
+      if (v > 0.0) {
+        lastpos = c;
+        if (first != INT32_MAX && run + v > target) {
+          s_c = (int32_t)c;
+          s_local = target - run;
           break;
         }
       }
-      C += r;
+      run += v;
     }
-    if (pick < 0 && last >= 0) {  // u >= 1 or rounding at the very end: last positive slice
-      pick = last;
-      local = INFINITY;
+    if (s_c < 0) {
+      s_c = (int32_t)lastpos;
+      s_local = INFINITY;
     }
-    sh_split = pick;
-    sh_target = local;
-    sh_R = R;
-    sh_token = -1;
   }
   __syncthreads();
-  const int32_t split = sh_split;
-  double range_total = 0.0;
-  int32_t tok;
-  double mass;
-  if (split >= 0) {
-    const int64_t lo = (int64_t)split * P.split_len_r;
-    const int64_t hi = lo + P.split_len_r < P.V ? lo + P.split_len_r : P.V;
-    tok = st.mode == kModeResidual
-              ? draw_in_range<DT, VEC, kModeResidual>(tr, dr, lo / W, hi / W, st, sh_target,
-                                                      false, u, range_total)
-              : draw_in_range<DT, VEC, kModeBonus>(tr, dr, lo / W, hi / W, st, sh_target,
-                                                   false, u, range_total);
-    mass = sh_R / st.st;
+  const int32_t csel = s_c;
+  if (csel >= 0) {
+    if (wave == 0) {
+      // The chunk's 64 units: a wavefront scan picks the unit, its lane walks the elements.
+      // With no crossing (u at the far end), the last unit with mass is taken.
+      const int64_t uu = (int64_t)csel * 64 + lane;
+      float r[W];
+      float us = 0.f;
+      if (uu < nunits) us = resid_unit<DT, VEC>(tr, dr, uu, st, r);
+      const double local = s_local;
+      const double incl = wave_incl_scan((double)us);
+      const uint64_t cross = __ballot(us > 0.f && incl > local);
+      const uint64_t pos = __ballot(us > 0.f);
+      const int32_t pl = cross ? __ffsll((long long)cross) - 1
+                               : (pos ? 63 - __clzll((long long)pos) : -1);
+      if (lane == pl) {
+        double run = incl - (double)us;
+        int32_t tok = -1, lastpos = -1;
+        for (int e = 0; e < W; ++e) {
+          if (r[e] > 0.f) {
+            lastpos = (int32_t)(uu * W + e);
+            run += (double)r[e];
+            if (cross && tok < 0 && run > local) tok = lastpos;
+          }
+        }
+        s_tok = tok >= 0 ? tok : lastpos;
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      P.out_tokens[tbase + j] = s_tok;
+      if (P.resid_mass) P.resid_mass[b] = R / st.st;
+    }
   } else {
-    // Empty residual (p <= q everywhere after rounding): draw from p_j over the whole row.
-    tok = draw_in_range<DT, VEC, kModeBonus>(tr, dr, 0, P.V / W, st, 0.0, true, u,
-                                             range_total);
-    mass = range_total / st.st;
-  }
-  if (tok >= 0) sh_token = tok;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    P.out_tokens[tbase + st.j] = sh_token;
-    if (P.resid_mass) P.resid_mass[b] = mass;
+    // Empty residual after rounding: fall back to a draw from p_j.
+    Stop sp = st;
+    sp.mode = kModeBonus;
+    double tot;
+    const int32_t tok = draw_from_row<DT>(tr, P.V, sp, u, shd, shi, tot);
+    if (tok >= 0) s_tok = tok;
+    __syncthreads();
+    if (tid == 0) {
+      P.out_tokens[tbase + j] = s_tok;
+      if (P.resid_mass) P.resid_mass[b] = tot / st.st;
+    }
   }
 }
 
@@ -698,40 +863,43 @@ __global__ __launch_bounds__(kThreads) void k_sample(Params P) {
 
 struct Plan {
   int32_t spr, nsplit, nsplit_r;
-  int64_t split_len, split_len_r;
-  size_t off_parts, off_stop, off_rsum, total;
+  int64_t split_len, chunk_stride;
+  size_t off_parts, off_stop, off_chunks, total;
 };
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
-
-// Slices per row: at least one full pass of the block's loads per slice where V allows,
-// more slices when there are too few rows to give every CU work.
-void choose_splits(int64_t rows, int64_t V, int W, int32_t &nsplit, int64_t &split_len) {
-  const int64_t units = (V + W - 1) / W;
-  int64_t ns = (units + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
-  if (rows * ns < kTargetWorkgroups) ns = (kTargetWorkgroups + rows - 1) / rows;
-  const int64_t cap = units / kMinUnitsPerSplit > 1 ? units / kMinUnitsPerSplit : 1;
-  if (ns > cap) ns = cap;
-  if (ns > kMaxSplits) ns = kMaxSplits;
-  if (ns < 1) ns = 1;
-  const int64_t per = (units + ns - 1) / ns;
-  ns = (units + per - 1) / per;  // no empty slice
-  nsplit = (int32_t)ns;
-  split_len = per * W;
-}
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool make_plan(int32_t B, int32_t gamma, int64_t V, int dtype, bool greedy, Plan &pl) {
-  if (B < 0 || gamma < 0 || gamma > SPEC_MAX_GAMMA || V < 1 || V > INT32_MAX) return false;
+  if (B < 0 || gamma < 0 || gamma > SPEC_MAX_GAMMA || V < 1 || V > kMaxV) return false;
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return false;
-  const int W = dtype == SPEC_F32 ? 4 : 8;
-  pl.spr = greedy ? gamma + 1 : 2 * gamma + 1;
   const int64_t bb = B > 0 ? B : 1;
-  choose_splits(bb * pl.spr, V, W, pl.nsplit, pl.split_len);
-  choose_splits(bb * 2, V, W, pl.nsplit_r, pl.split_len_r);
+  pl.spr = greedy ? gamma + 1 : 2 * gamma + 1;
+  const int64_t rows = bb * (gamma + 1 + (greedy ? 0 : gamma));
+  // k_rowstats: one tile per workgroup; small problems get finer (partial) tiles.
+  const int64_t tiles = ceil_div(V, kTileElems);
+  const int64_t ns = tiles;
+  int64_t len = kTileElems;
+  if (tiles * rows < kSmallGrid && tiles < kMaxSlices) {
+    int64_t want = ceil_div(kSmallGrid, rows);
+    const int64_t cap = ceil_div(V, 2048);
+    if (want > cap) want = cap;
+    if (want > kMaxSlices) want = kMaxSlices;
+    if (want > ns) len = ceil_div(ceil_div(V, want), 8) * 8;
+  }
+  pl.nsplit = (int32_t)ceil_div(V, len);  // no empty slice
+  pl.split_len = len;
+  // k_resid: enough workgroups per request to spread the stop rows over the GPU.
+  pl.chunk_stride = ceil_div(V, 64);       // chunks per row on the element path (the most)
+  const int64_t vec_chunks = ceil_div(ceil_div(V, dtype == SPEC_F32 ? 4 : 8), 64);
+  int64_t nsr = ceil_div(kResidGrid, bb);
+  if (nsr > vec_chunks) nsr = vec_chunks;
+  if (nsr < 1) nsr = 1;
+  pl.nsplit_r = greedy ? 1 : (int32_t)nsr;
   pl.off_parts = 0;
   pl.off_stop = align_up((size_t)bb * pl.spr * pl.nsplit * sizeof(Partial));
-  pl.off_rsum = pl.off_stop + align_up((size_t)bb * sizeof(Stop));
-  pl.total = pl.off_rsum + align_up((size_t)bb * pl.nsplit_r * sizeof(double));
+  pl.off_chunks = pl.off_stop + align_up((size_t)bb * sizeof(Stop));
+  pl.total = pl.off_chunks + (greedy ? 0 : align_up((size_t)bb * pl.chunk_stride * sizeof(double)));
   return true;
 }
 
@@ -741,73 +909,65 @@ int record(const spec_probe *probe, int k, hipStream_t s) {
                                                                        : SPEC_ERR_HIP;
 }
 
-#define SPEC_TRY(expr)            \
-  do {                            \
-    const int rc_ = (expr);       \
+#define SPEC_TRY(expr)              \
+  do {                              \
+    const int rc_ = (expr);         \
     if (rc_ != SPEC_OK) return rc_; \
   } while (0)
 
 int launched() { return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP; }
 
 template <int DT, bool VEC>
-int run_sample(const Params &P, const Plan &pl, const spec_probe *probe, hipStream_t s) {
-  const int64_t g1 = (int64_t)P.B * pl.spr * pl.nsplit;
-  const int64_t g3 = (int64_t)P.B * pl.nsplit_r;
+int run(const Params &P, const Plan &pl, const spec_probe *probe, hipStream_t s, bool greedy) {
+  const int64_t slots = (int64_t)P.B * pl.spr;
+  const uint32_t gy = (uint32_t)(slots < kMaxGridY ? slots : kMaxGridY);
+  const uint32_t gz = (uint32_t)ceil_div(slots, gy);
   SPEC_TRY(record(probe, 0, s));
-  k_rowstats<DT, VEC><<<dim3((uint32_t)g1), dim3(kThreads), 0, s>>>(P);
+  k_rowstats<DT, VEC><<<dim3((uint32_t)pl.nsplit, gy, gz), dim3(kThreads), 0, s>>>(P);
   SPEC_TRY(launched());
   SPEC_TRY(record(probe, 1, s));
   SPEC_TRY(record(probe, 2, s));
-  k_decide<DT><<<dim3((uint32_t)((P.B + kWaves - 1) / kWaves)), dim3(kThreads), 0, s>>>(P);
+  k_resid<DT, VEC><<<dim3((uint32_t)((int64_t)P.B * pl.nsplit_r)), dim3(kThreads), 0, s>>>(P);
   SPEC_TRY(launched());
   SPEC_TRY(record(probe, 3, s));
-  SPEC_TRY(record(probe, 4, s));
-  k_resid<DT, VEC><<<dim3((uint32_t)g3), dim3(kThreads), 0, s>>>(P);
-  SPEC_TRY(launched());
-  SPEC_TRY(record(probe, 5, s));
-  SPEC_TRY(record(probe, 6, s));
-  k_sample<DT, VEC><<<dim3((uint32_t)P.B), dim3(kThreads), 0, s>>>(P);
-  SPEC_TRY(launched());
-  SPEC_TRY(record(probe, 7, s));
-  return SPEC_OK;
-}
-
-template <int DT, bool VEC>
-int run_greedy(const Params &P, const Plan &pl, const spec_probe *probe, hipStream_t s) {
-  const int64_t g1 = (int64_t)P.B * pl.spr * pl.nsplit;
-  SPEC_TRY(record(probe, 0, s));
-  k_rowstats<DT, VEC><<<dim3((uint32_t)g1), dim3(kThreads), 0, s>>>(P);
-  SPEC_TRY(launched());
-  SPEC_TRY(record(probe, 1, s));
-  SPEC_TRY(record(probe, 2, s));
-  k_decide<DT><<<dim3((uint32_t)((P.B + kWaves - 1) / kWaves)), dim3(kThreads), 0, s>>>(P);
-  SPEC_TRY(launched());
-  SPEC_TRY(record(probe, 3, s));
+  if (!greedy) {
+    SPEC_TRY(record(probe, 4, s));
+    k_draw<DT, VEC><<<dim3((uint32_t)P.B), dim3(kThreads), 0, s>>>(P);
+    SPEC_TRY(launched());
+    SPEC_TRY(record(probe, 5, s));
+  }
   return SPEC_OK;
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-int common_checks(int32_t B, int32_t gamma, int64_t V, int dtype, void *workspace,
-                  size_t workspace_bytes, const Plan &pl, int64_t grid1) {
-  (void)B; (void)gamma; (void)V; (void)dtype;
-  if (!workspace) return SPEC_ERR_NULL;
-  if (((uintptr_t)workspace & (kAlign - 1)) != 0 || workspace_bytes < pl.total)
-    return SPEC_ERR_WORKSPACE;
-  if (grid1 > (int64_t)UINT32_MAX) return SPEC_ERR_SHAPE;
+int check_shape(int32_t B, int32_t gamma, int64_t V, int dtype) {
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_DTYPE;
+  if (B < 0 || gamma < 0 || gamma > SPEC_MAX_GAMMA || V < 1 || V > kMaxV) return SPEC_ERR_SHAPE;
   return SPEC_OK;
 }
 
-void fill_workspace(Params &P, const Plan &pl, void *workspace) {
+int setup(Params &P, const Plan &pl, void *workspace, size_t workspace_bytes) {
+  if (!workspace) return SPEC_ERR_NULL;
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0 || workspace_bytes < pl.total)
+    return SPEC_ERR_WORKSPACE;
+  if ((int64_t)P.B * pl.nsplit_r > (int64_t)UINT32_MAX) return SPEC_ERR_SHAPE;
   char *ws = static_cast<char *>(workspace);
   P.parts = reinterpret_cast<Partial *>(ws + pl.off_parts);
   P.stop = reinterpret_cast<Stop *>(ws + pl.off_stop);
-  P.rsum = reinterpret_cast<double *>(ws + pl.off_rsum);
+  P.chunk_sums = reinterpret_cast<double *>(ws + pl.off_chunks);
+  P.chunk_stride = pl.chunk_stride;
   P.spr = pl.spr;
   P.nsplit = pl.nsplit;
   P.split_len = pl.split_len;
   P.nsplit_r = pl.nsplit_r;
-  P.split_len_r = pl.split_len_r;
+  return SPEC_OK;
+}
+
+template <int DT>
+int dispatch(const Params &P, const Plan &pl, const spec_probe *probe, hipStream_t s, bool vec,
+             bool greedy) {
+  return vec ? run<DT, true>(P, pl, probe, s, greedy) : run<DT, false>(P, pl, probe, s, greedy);
 }
 
 }  // namespace
@@ -825,7 +985,8 @@ const char *spec_verify_strerror(int code) {
   switch (code) {
     case SPEC_OK: return "success";
     case SPEC_ERR_NULL: return "a required pointer is NULL";
-    case SPEC_ERR_SHAPE: return "invalid sizes (B < 0, gamma outside [0, 64], V outside [1, 2^31-1], or grid too large)";
+    case SPEC_ERR_SHAPE:
+      return "invalid sizes (B < 0, gamma outside [0, 64], V outside [1, 2^24], or grid too large)";
     case SPEC_ERR_DTYPE: return "dtype is neither SPEC_F32 nor SPEC_BF16";
     case SPEC_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
     case SPEC_ERR_HIP: return "HIP kernel launch or event record failed";
@@ -839,19 +1000,13 @@ int spec_verify_sample(const void *target_logits, const void *draft_logits, int 
                        const int32_t *cu_draft, int64_t V, int32_t *out_tokens,
                        int32_t *out_num_accepted, void *workspace, size_t workspace_bytes,
                        const spec_probe *probe, void *stream) {
-  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_DTYPE;
-  if (B < 0 || gamma < 0 || gamma > SPEC_MAX_GAMMA || V < 1 || V > INT32_MAX)
-    return SPEC_ERR_SHAPE;
+  SPEC_TRY(check_shape(B, gamma, V, dtype));
   if (B == 0) return SPEC_OK;
   if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !temperatures ||
       !out_tokens || !out_num_accepted)
     return SPEC_ERR_NULL;
   Plan pl;
   if (!make_plan(B, gamma, V, dtype, false, pl)) return SPEC_ERR_SHAPE;
-  const int64_t grid1 = (int64_t)B * pl.spr * pl.nsplit;
-  SPEC_TRY(common_checks(B, gamma, V, dtype, workspace, workspace_bytes, pl, grid1));
-  if ((int64_t)B * pl.nsplit_r > (int64_t)UINT32_MAX) return SPEC_ERR_SHAPE;
-
   Params P = {};
   P.target = target_logits;
   P.draft = draft_logits;
@@ -865,7 +1020,7 @@ int spec_verify_sample(const void *target_logits, const void *draft_logits, int 
   P.out_tokens = out_tokens;
   P.out_n = out_num_accepted;
   P.greedy_all = 0;
-  fill_workspace(P, pl, workspace);
+  SPEC_TRY(setup(P, pl, workspace, workspace_bytes));
   if (probe) {
     P.p_x = probe->p_x;
     P.q_x = probe->q_x;
@@ -878,28 +1033,19 @@ int spec_verify_sample(const void *target_logits, const void *draft_logits, int 
   const int es = dtype == SPEC_F32 ? 4 : 2;
   const bool vec = aligned16(target_logits) && aligned16(draft_logits) && (V * es) % 16 == 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == SPEC_F32)
-    return vec ? run_sample<SPEC_F32, true>(P, pl, probe, s)
-               : run_sample<SPEC_F32, false>(P, pl, probe, s);
-  return vec ? run_sample<SPEC_BF16, true>(P, pl, probe, s)
-             : run_sample<SPEC_BF16, false>(P, pl, probe, s);
+  return dtype == SPEC_F32 ? dispatch<SPEC_F32>(P, pl, probe, s, vec, false)
+                           : dispatch<SPEC_BF16>(P, pl, probe, s, vec, false);
 }
 
 int spec_verify_greedy(const void *target_logits, int dtype, const int32_t *draft_tokens,
                        int32_t B, int32_t gamma, const int32_t *cu_draft, int64_t V,
                        int32_t *out_tokens, int32_t *out_num_accepted, void *workspace,
                        size_t workspace_bytes, const spec_probe *probe, void *stream) {
-  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_DTYPE;
-  if (B < 0 || gamma < 0 || gamma > SPEC_MAX_GAMMA || V < 1 || V > INT32_MAX)
-    return SPEC_ERR_SHAPE;
+  SPEC_TRY(check_shape(B, gamma, V, dtype));
   if (B == 0) return SPEC_OK;
-  if (!target_logits || !draft_tokens || !out_tokens || !out_num_accepted)
-    return SPEC_ERR_NULL;
+  if (!target_logits || !draft_tokens || !out_tokens || !out_num_accepted) return SPEC_ERR_NULL;
   Plan pl;
   if (!make_plan(B, gamma, V, dtype, true, pl)) return SPEC_ERR_SHAPE;
-  const int64_t grid1 = (int64_t)B * pl.spr * pl.nsplit;
-  SPEC_TRY(common_checks(B, gamma, V, dtype, workspace, workspace_bytes, pl, grid1));
-
   Params P = {};
   P.target = target_logits;
   P.draft = nullptr;
@@ -911,16 +1057,13 @@ int spec_verify_greedy(const void *target_logits, int dtype, const int32_t *draf
   P.out_tokens = out_tokens;
   P.out_n = out_num_accepted;
   P.greedy_all = 1;
-  fill_workspace(P, pl, workspace);
+  SPEC_TRY(setup(P, pl, workspace, workspace_bytes));
   if (probe) P.row_max_t = probe->row_max_t;
   const int es = dtype == SPEC_F32 ? 4 : 2;
   const bool vec = aligned16(target_logits) && (V * es) % 16 == 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == SPEC_F32)
-    return vec ? run_greedy<SPEC_F32, true>(P, pl, probe, s)
-               : run_greedy<SPEC_F32, false>(P, pl, probe, s);
-  return vec ? run_greedy<SPEC_BF16, true>(P, pl, probe, s)
-             : run_greedy<SPEC_BF16, false>(P, pl, probe, s);
+  return dtype == SPEC_F32 ? dispatch<SPEC_F32>(P, pl, probe, s, vec, true)
+                           : dispatch<SPEC_BF16>(P, pl, probe, s, vec, true);
 }
 
 }  // extern "C"

@@ -65,6 +65,17 @@ def test_many_requests_peaked_rows():
     assert rep["ambiguous"] <= 0.1 * rep["sampled"]
 
 
+def test_long_rows_with_multi_tile_slices():
+    # rows long enough that one slice holds several row-statistics tiles (bf16, > 64 tiles)
+    # and several residual tiles (fp32, > 64 residual tiles), with ragged tails
+    w = workloads.small(B=2, gamma=2, V=1_100_003 - 3, dtype="bf16", seed=31,
+                        temperatures=np.array([0.9, 0.0]), draft_sigma=0.6)
+    _both(w)
+    w = workloads.small(B=2, gamma=3, V=600_000, dtype="f32", seed=32,
+                        temperatures=np.array([1.1, 0.5]), draft_sigma=0.6)
+    _both(w)
+
+
 # ----------------------------------------------------------------------- edge cases
 
 def test_p_equal_q_accepts_everything_on_gpu():
@@ -125,8 +136,19 @@ def test_single_token_vocabulary():
 
 
 def test_extreme_temperatures():
+    # tiny and huge T; with logits near +-10 the smaller temperatures take the row
+    # statistics' overflow-safe exponent form, the others the two-FMA form
     temps = np.array([1e-30, 1e-6, 1e-3, 50.0, 1e4, 0.0], dtype=np.float32)
     w = workloads.small(B=6, gamma=4, V=2048, dtype="bf16", seed=8, temperatures=temps)
+    _both(w)
+
+
+def test_large_logits():
+    # logits of magnitude ~1e4 at T = 1: |max| c is above the two-FMA limit
+    w = workloads.small(B=4, gamma=3, V=3000, dtype="f32", seed=9, temperatures=1.0,
+                        target_sigma=1.0, draft_sigma=0.5)
+    w.target += np.float32(-2.0e4)
+    w.draft += np.float32(-2.0e4)
     _both(w)
 
 
