@@ -30,7 +30,8 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MALL_BYTES = 256 << 20          # last-level (Infinity) cache
 KERNELS = ["k_rowstats", "k_resid", "k_draw"]
 DEFAULT_WORKLOAD = 5
-TRAFFIC_FILE = ROOT / "profiles" / "traffic_k_rowstats.json"
+PROFILES = ROOT / "profiles"
+COPY_BYTES = 1 << 30            # plain copy used to calibrate the HBM byte counters
 KERNEL_SRC = ROOT / "speculative_sampling_verification_spec_amd" / "csrc" / "spec_verify.hip"
 
 
@@ -66,16 +67,29 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def traffic_for_current_kernel():
-    """HBM bytes per k_rowstats launch from the committed rocprofv3 counter runs, or None if
-    the kernel source changed since they were taken."""
-    if not TRAFFIC_FILE.exists():
+def traffic_for_current_kernel(workload: int):
+    """HBM bytes per k_rowstats launch from the committed rocprofv3 counter runs for this
+    workload, or None if there are none or the kernel source changed since they were taken."""
+    path = PROFILES / f"k_rowstats_workload{workload}_traffic.json"
+    if not path.exists():
         return None
-    rec = json.loads(TRAFFIC_FILE.read_text())
+    rec = json.loads(path.read_text())
     sha = hashlib.sha256(KERNEL_SRC.read_bytes()).hexdigest()
     if rec.get("source_sha256") != sha:
         return None
     return rec
+
+
+def copy_calibration():
+    """A plain device-to-device copy of COPY_BYTES, the reference the HBM byte counters
+    (FETCH_SIZE, WRITE_SIZE) are scaled by."""
+    import torch
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "dispatches": 5}), flush=True)
 
 
 def cpu_baseline(w, target_seconds: float):
@@ -107,6 +121,8 @@ def main():
                     help="1..5; the JSON line is for workload 5 by default")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the plain copy the byte counters are calibrated with")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -121,6 +137,9 @@ def main():
     import speculative_sampling_verification_spec_amd as sv
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     t_gen = time.perf_counter()
     w = workloads.config(args.workload)
     print(f"[bench] generated workload {args.workload} in {time.perf_counter() - t_gen:.1f} s",
@@ -164,7 +183,7 @@ def main():
 
     rs_us = per_kernel_us["k_rowstats"]
     achieved = nbytes / (rs_us * 1e-6) / 1e9
-    traffic = traffic_for_current_kernel()
+    traffic = traffic_for_current_kernel(args.workload)
     positions = w.positions
     value = positions / (ms_per_step * 1e-3)
     logit_gbps = nbytes / (ms_per_step * 1e-3) / 1e9

@@ -37,9 +37,8 @@
  * at cu_draft[b] + b (dense: b*(gamma+1)).  R_t = total target rows = R_d + B.
  *
  * Ownership.  The caller allocates and owns every buffer (device memory unless stated),
- * including the workspace.  The library allocates nothing and keeps nothing between calls
- * except, per device, the size of its persistent grid (a property of the device and the
- * kernel); it is reentrant for distinct workspaces and touches only the ranges described.  Calls are
+ * including the workspace.  The library allocates nothing, keeps no state between calls,
+ * is reentrant for distinct workspaces, and touches only the ranges described.  Calls are
  * asynchronous on `stream` (a hipStream_t; NULL is the null stream) and never wait for the
  * device.  Two calls may share a workspace only when ordered on one stream.
  *
