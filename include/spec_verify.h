@@ -90,8 +90,9 @@ typedef struct spec_probe {
                          (= 1) for the bonus; sampled requests                            */
   void *events[8];    /* host: hipEvent_t or NULL; events[2k] / events[2k+1] are recorded on
                          `stream` just before / after the k-th kernel launch of the call
-                         (sample: 0 row statistics, 1 decide + residual sums, 2 draw;
-                          greedy: 0 row argmax, 1 decide)                                */
+                         (launch 0: row statistics; then either launch 1: accept tests,
+                         residual and draw in one, or launch 1: accept tests and residual,
+                         launch 2: draw); entries past the last launch are not touched  */
 } spec_probe;
 
 /*

@@ -5,32 +5,35 @@
 // and emit a draw from max(p_j - q_j, 0) there, or from p_gamma when nothing was rejected;
 // at temperature zero, compare each draft with the target argmax instead.
 //
-// Three launches on the caller's stream, none of which waits for the host:
+// Two or three launches on the caller's stream, none of which waits for the host:
 //
 //  k_rowstats  The HBM-bound stream.  Every needed logit row is read exactly once, cut into
 //              16K-element tiles, one workgroup per (row slot, slice) on a 2-D grid; slots a
 //              request does not use exit at once.  The workgroup loads its tile with 16-byte
-//              nontemporal loads straight into registers, takes the tile maximum (wave
-//              shuffles + one LDS exchange), then sums 2^((z - M) c), c = log2(e)/T, with fp32
-//              terms added pairwise per 16-byte unit and fp64 accumulation.  Greedy rows
-//              (T = 0) reduce to (max, lowest argmax).  Output: one partial per (row, slice).
+//              nontemporal loads straight into registers, takes the tile maximum (packed
+//              16-bit integer compares for bf16, wave shuffles, one LDS exchange), then sums
+//              2^((z - M) c), c = log2(e)/T: fp32 terms in a fixed pairwise tree over each
+//              thread's 64 elements, fp64 beyond.  Greedy rows (T = 0) reduce to (max, lowest
+//              argmax).  Output: one partial per (row, slice), and the row's logit at its
+//              draft token from the tile that holds it.
 //
-//  k_resid     Workgroups (request, residual slice).  Each merges its request's row partials
-//              (one wavefront per row, one lane per slice, fp64), runs the accept tests
-//              lane-parallel (p(x), q(x) in fp64 from the two gathered logits) and finds the
-//              first rejection with ballot + find-first-set; slice 0 writes the outputs.  A
-//              sampled request's workgroups then stream their slice of the stop row(s) again
-//              and write one fp64 sum of S_t (p_k - q_k)_+ (or S_t p_k for the bonus) per
-//              64-unit chunk.
+// Then a request is finished in four steps: (1) merge its row partials (one wavefront per
+// row, one lane per slice, fp64); (2) run the accept tests lane-parallel (p(x), q(x) in fp64
+// from the captured logits) and find the first rejection with ballot + find-first-set, write
+// the outputs; (3) stream the stop row(s) once more into one fp64 sum of S_t (p_k - q_k)_+
+// (or S_t p_k for the bonus) per 64-unit chunk; (4) draw: a block scan over the chunk sums
+// picks the chunk holding u * R, a wavefront scan over its 64 units picks the unit, and a walk
+// over the unit's elements gives the token.  Two ways, chosen per call by size:
 //
-//  k_draw      One workgroup per sampled request: a block scan over the chunk sums picks the
-//              chunk holding u * R, a wavefront scan over its 64 units picks the unit, and a
-//              walk over the unit's elements gives the token.
+//  k_finish    (many requests) one workgroup per request does steps 1-4.
+//  k_resid     (few requests with long rows) workgroups (request, 1024-unit slice of the stop
+//              row) each repeat steps 1-2 and stream their slice (step 3); then
+//  k_draw      one workgroup per request draws (step 4).
 //
 // Numerics: logits convert exactly to fp32; exponent arguments carry the temperature as a
 // two-float constant, so rounding never shifts the temperature, and their shifts are kept
-// exact in fp64 when partials are combined; every sum beyond a 16-byte unit is fp64.  Merged
-// row sums are the oracle's normaliser sum_k exp((z_k - max)/T).
+// exact in fp64 when partials are combined; every sum beyond one thread's terms is fp64.
+// Merged row sums are the normaliser sum_k exp((z_k - max)/T).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -47,9 +50,9 @@ constexpr int kWaves = kThreads / 64;
 constexpr int64_t kTileElems = 16384;        // k_rowstats tile: 64 elements per thread
 constexpr int kMaxSlices = 64;               // finest cut of rows in small problems
 constexpr int kSmallGrid = 1024;             // below this many tiles, cut rows finer
-constexpr int kResidGrid = 2048;             // k_resid workgroups aimed for
 constexpr int64_t kMaxGridY = 65535;         // k_rowstats slots per grid row (y), z covers more
-constexpr int kResChunksInFlight = 8;        // 64-unit chunks per wavefront per iteration
+constexpr int kFinPassUnits = 4096;         // k_finish: stop-row units per pass in flight
+constexpr int kResSliceUnits = 1024;         // k_resid: stop-row units per workgroup
 constexpr int64_t kMaxV = int64_t(1) << 24;
 constexpr double kLog2e = 1.4426950408889634074;
 constexpr size_t kAlign = 256;
@@ -67,14 +70,16 @@ struct alignas(16) Partial {
 
 enum : int32_t { kModeNone = 0, kModeResidual = 1, kModeBonus = 2 };
 
-// The stop row of a sampled request, written by k_resid for k_draw.
+// What the residual weights and the draw of a sampled request's stop row j need; on the
+// split path k_resid leaves it in the workspace for k_draw.
 struct alignas(16) Stop {
-  int32_t j, mode;
-  float mt, md;              // raw maxima of target / draft row j
+  int32_t mode;
+  float mt, md;              // maxima of target / draft row j
   float c_hi, c_lo;          // log2(e)/T as a two-float constant
   float rho_hi, rho_lo;      // S_t / S_d as a two-float constant
   double st;                 // S_t
-  double pad;
+  int64_t trow;              // target row j: also the output slot of the emitted token
+  int64_t drow;              // draft row j (read in residual mode only)
 };
 
 struct Params {
@@ -86,13 +91,14 @@ struct Params {
   int64_t V;
   int32_t *out_tokens, *out_n;
   Partial *parts;
-  Stop *stop;
+  float *gz;                // [B][spr] logit of each sampled row at its row's draft token
+  Stop *stop;               // [B] split path: stop records from k_resid for k_draw
+  int32_t nsplit_r;         // split path: k_resid workgroups per request
   double *chunk_sums;       // [B][chunk_stride] residual sums per 64-unit chunk
   int64_t chunk_stride;
   int32_t spr;              // row slots per request: 2*gamma+1 (sample) or gamma+1 (greedy)
   int32_t nsplit;           // k_rowstats tiles (slices) per row
   int64_t split_len;        // elements per slice: one tile, or less for small problems
-  int32_t nsplit_r;         // k_resid workgroups per request
   int32_t greedy_all;
   double *p_x, *q_x, *row_sum_t, *row_sum_d, *resid_mass;
   float *row_max_t, *row_max_d;
@@ -163,8 +169,7 @@ struct Unit {
       return __uint_as_float((uint32_t)base[u] << 16);
     }
   }
-  // Filler for units past the row end: the most negative finite value (both bf16 halves;
-  // a word read as fp32 must not be a NaN for max_raw below).
+  // Filler for units past the row end: the most negative finite value (its term is 0).
   __device__ static __forceinline__ Raw filler() {
     if constexpr (VEC) {
       const uint32_t v = DT == SPEC_F32 ? 0xff7fffffu : 0xff7fff7fu;
@@ -173,27 +178,46 @@ struct Unit {
       return DT == SPEC_F32 ? -3.40282347e38f : __uint_as_float(0xff7f0000u);
     }
   }
-  // Running maximum over a unit without unpacking bf16 high halves.  A 32-bit word read as
-  // fp32 sorts between its high bf16 value (inclusive) and the next bf16 value away from
-  // zero (exclusive), so its order against every other bf16 value is kept, and clearing the
-  // low 16 bits of the maximum (exact_max) gives the exact maximum.
-  __device__ static __forceinline__ float max_raw(const Raw &r, float m) {
-    if constexpr (!VEC) {
-      return fmaxf(m, r);
-    } else if constexpr (DT == SPEC_F32) {
-      return fmaxf(fmaxf(m, __uint_as_float(r.x)),
-                   fmaxf(fmaxf(__uint_as_float(r.y), __uint_as_float(r.z)), __uint_as_float(r.w)));
+  // Exact maximum over a thread's units.  bf16 pairs are compared as packed 16-bit integers,
+  // one instruction per pair and no conversion: read as int16, bf16 patterns order every
+  // non-negative value correctly and place every negative value below them; among patterns
+  // with the sign bit set, the smallest unsigned pattern is the largest value.  So a
+  // non-negative signed maximum is the maximum, and otherwise (all values negative) the
+  // unsigned minimum is.
+  template <int N>
+  __device__ static __forceinline__ float thread_max(const Raw (&r)[N]) {
+    if constexpr (VEC && DT == SPEC_BF16) {
+      typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
+      typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+      i16x2 mi = {INT16_MIN, INT16_MIN};
+      u16x2 mu = {UINT16_MAX, UINT16_MAX};
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        const uint32_t w[4] = {r[j].x, r[j].y, r[j].z, r[j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          mi = __builtin_elementwise_max(mi, __builtin_bit_cast(i16x2, w[q]));
+          mu = __builtin_elementwise_min(mu, __builtin_bit_cast(u16x2, w[q]));
+        }
+      }
+      const int16_t smax = mi.x > mi.y ? mi.x : mi.y;
+      const uint16_t umin = mu.x < mu.y ? mu.x : mu.y;
+      const uint32_t pat = smax >= 0 ? (uint32_t)(uint16_t)smax : (uint32_t)umin;
+      return __uint_as_float(pat << 16);
     } else {
-      m = fmaxf(m, fmaxf(__uint_as_float(r.x << 16), __uint_as_float(r.x)));
-      m = fmaxf(m, fmaxf(__uint_as_float(r.y << 16), __uint_as_float(r.y)));
-      m = fmaxf(m, fmaxf(__uint_as_float(r.z << 16), __uint_as_float(r.z)));
-      m = fmaxf(m, fmaxf(__uint_as_float(r.w << 16), __uint_as_float(r.w)));
+      float m = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        if constexpr (!VEC) {
+          m = fmaxf(m, r[j]);
+        } else {
+          m = fmaxf(fmaxf(m, __uint_as_float(r[j].x)),
+                    fmaxf(fmaxf(__uint_as_float(r[j].y), __uint_as_float(r[j].z)),
+                          __uint_as_float(r[j].w)));
+        }
+      }
       return m;
     }
-  }
-  __device__ static __forceinline__ float exact_max(float m) {
-    if constexpr (VEC && DT == SPEC_BF16) return __uint_as_float(__float_as_uint(m) & 0xffff0000u);
-    else return m;
   }
   __device__ static __forceinline__ void cvt(const Raw &r, float (&x)[W]) {
     if constexpr (!VEC) {
@@ -320,6 +344,7 @@ __device__ __forceinline__ int32_t block_min1(int32_t v, int32_t *sh) {
 
 // Exclusive scan over the block in thread order (fp64); also returns the block total.
 // Ends with a barrier so `sh` can be reused at once.
+template <int NW>
 __device__ double block_excl_scan(double v, double *sh, double &total) {
   const int w = threadIdx.x >> 6;
   const double inc = wave_incl_scan(v);
@@ -328,7 +353,7 @@ __device__ double block_excl_scan(double v, double *sh, double &total) {
   double off = 0.0;
   total = 0.0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
+  for (int i = 0; i < NW; ++i) {
     if (i < w) off += sh[i];
     total += sh[i];
   }
@@ -337,6 +362,7 @@ __device__ double block_excl_scan(double v, double *sh, double &total) {
 }
 
 // First / last thread (by id) for which `pred` holds, block-wide: INT32_MAX / -1 if none.
+template <int NW>
 __device__ int32_t block_first(bool pred, int32_t *sh) {
   const uint64_t m = __ballot(pred);
   if ((threadIdx.x & 63) == 0)
@@ -344,10 +370,11 @@ __device__ int32_t block_first(bool pred, int32_t *sh) {
   __syncthreads();
   int32_t r = INT32_MAX;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) r = sh[i] < r ? sh[i] : r;
+  for (int i = 0; i < NW; ++i) r = sh[i] < r ? sh[i] : r;
   __syncthreads();
   return r;
 }
+template <int NW>
 __device__ int32_t block_last(bool pred, int32_t *sh) {
   const uint64_t m = __ballot(pred);
   if ((threadIdx.x & 63) == 0)
@@ -355,7 +382,7 @@ __device__ int32_t block_last(bool pred, int32_t *sh) {
   __syncthreads();
   int32_t r = -1;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) r = sh[i] > r ? sh[i] : r;
+  for (int i = 0; i < NW; ++i) r = sh[i] > r ? sh[i] : r;
   __syncthreads();
   return r;
 }
@@ -390,16 +417,20 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Params P) {
   request(P, b, dbase, gb, T);
   const void *base;
   int64_t row;
+  int32_t pos;  // draft position whose token this row is tested at; gb for the bonus row
   if (k <= P.gamma) {
     if (k > gb) return;
     base = P.target;
     row = dbase + b + k;
+    pos = k;
   } else {
     const int32_t i = k - P.gamma - 1;
     if (i >= gb || !(T > 0.f)) return;
     base = P.draft;
     row = dbase + i;
+    pos = i;
   }
+  const int32_t tok = T > 0.f && pos < gb ? P.tokens[dbase + pos] : -1;
   const int64_t lo = (int64_t)blockIdx.x * P.split_len;
   const int64_t hi = lo + P.split_len < P.V ? lo + P.split_len : P.V;
   const Store *tile = static_cast<const Store *>(row_ptr<DT>(base, row, P.V)) + lo / W;
@@ -417,33 +448,61 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Params P) {
       raw[j] = u < nu ? U::template load<true>(tile, u) : U::filler();
     }
   }
-  float tm = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < NV; ++j) tm = U::max_raw(raw[j], tm);
-  const float M = U::exact_max(block_max1(tm, sh.mx));
+  const float tm = U::thread_max(raw);
+  const float M = block_max1(tm, sh.mx);
   Partial *out = P.parts + (int64_t)slot * P.nsplit + blockIdx.x;
+
+  // The logit at the row's draft token, for k_resid's accept tests: written by the thread
+  // holding it, in the one tile that does.
+  if (tok >= lo && tok < hi) {
+    const int32_t off = (int32_t)(tok - lo);
+    const int32_t uo = off / W;
+    if (uo % kThreads == tid) {
+      float z = 0.f;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        if (j == uo / kThreads) {
+          float xv[W];
+          U::cvt(raw[j], xv);
+#pragma unroll
+          for (int q = 0; q < W; ++q)
+            if (q == off % W) z = xv[q];
+        }
+      }
+      P.gz[slot] = z;
+    }
+  }
 
   if (T > 0.f) {
     const TempConst tc = temp_const(T);
-    double acc = 0.0;
     if (fold_ok(M, tc.c_hi) && tc.c < 1e6 && tc.c > 1e-30) {
       // The common case: two-FMA exponent arguments.  In this range of c a filler's
       // argument is -inf or below -200, so its term is exactly 0 and needs no mask.
       const float K = (float)((double)M * tc.c);
+      // Unit sums, then a fixed pairwise tree over the thread's NV units in fp32: 64 terms
+      // of at most ~1.4 each, so the thread's sum carries at most ~6 roundings (3.6e-7
+      // relative); everything beyond the thread is fp64.
+      float us[NV];
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
         float x[W], e[W];
         U::cvt(raw[j], x);
 #pragma unroll
         for (int q = 0; q < W; ++q) e[q] = ex2(arg_folded(x[q], K, tc.c_hi, tc.c_lo));
-        acc += (double)unit_sum<W>(e);
+        us[j] = unit_sum<W>(e);
       }
-      const double S = block_sum1(acc, sh.sum);
+#pragma unroll
+      for (int st = 1; st < NV; st *= 2) {
+#pragma unroll
+        for (int j = 0; j + st < NV; j += 2 * st) us[j] += us[j + st];
+      }
+      const double S = block_sum1((double)us[0], sh.sum);
       // to the shifted form, sum 2^((z - M) c): factor 2^(K - M c), one rounding
       if (tid == 0) *out = Partial{M, 0, S * exp2(fma(-(double)M, tc.c, (double)K))};
     } else {
       // Extreme temperatures or logits: overflow-safe arguments, units re-read one at a time
       // (cache hits) to keep this rare path out of the common path's registers.
+      double acc = 0.0;
 #pragma unroll 1
       for (int j = 0; j < NV; ++j) {
         const int32_t u = j * kThreads + tid;
@@ -459,23 +518,26 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Params P) {
       if (tid == 0) *out = Partial{M, 0, S};
     }
   } else {
-    // Greedy row: the lowest index holding the tile maximum.
+    // Greedy row: the lowest index holding the tile maximum; only threads whose own maximum
+    // equals it search their units.
     int32_t ti = INT32_MAX;
+    if (tm == M) {
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      float x[W];
-      U::cvt(raw[j], x);
-      const int32_t u = j * kThreads + tid;
+      for (int j = 0; j < NV; ++j) {
+        float x[W];
+        U::cvt(raw[j], x);
+        const int32_t u = j * kThreads + tid;
 #pragma unroll
-      for (int q = 0; q < W; ++q)
-        if (ti == INT32_MAX && u < nu && x[q] == M) ti = (int32_t)((lo / W + u) * W + q);
+        for (int q = 0; q < W; ++q)
+          if (ti == INT32_MAX && u < nu && x[q] == M) ti = (int32_t)((lo / W + u) * W + q);
+      }
     }
     const int32_t bi = block_min1(ti, sh.idx);
     if (tid == 0) *out = Partial{M, bi, 0.0};
   }
 }
 
-// ------------------------------------------------------------------ k_resid
+// ------------------------------------------------------------------ finishing a request
 
 // Residual weight of one element of the stop row, scaled by S_t:
 //   residual mode: S_t (p_k - q_k)_+ = (e_t - rho e_d)_+ with rho = S_t / S_d (two-float);
@@ -495,201 +557,6 @@ __device__ __forceinline__ void resid_weights(const float (&zt)[W], const float 
     }
   }
 }
-
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_resid(Params P) {
-  using U = Unit<DT, VEC>;
-  using Store = typename U::Store;
-  constexpr int W = U::W;
-  constexpr int NC = kResChunksInFlight;
-  constexpr int kRows = 2 * SPEC_MAX_GAMMA + 1;
-  __shared__ float s_m[kRows];
-  __shared__ double s_s[kRows];
-  __shared__ int32_t s_i[SPEC_MAX_GAMMA + 1];
-  __shared__ int32_t s_j;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int32_t b = (int32_t)(blockIdx.x / P.nsplit_r);
-  const int32_t split = (int32_t)(blockIdx.x % P.nsplit_r);
-  int64_t dbase;
-  int32_t gb;
-  float T;
-  request(P, b, dbase, gb, T);
-  const bool sampling = T > 0.f;
-  if (!sampling && split != 0) return;  // one workgroup finishes a greedy request
-  const int64_t tbase = dbase + b;
-  const int32_t ntr = gb + 1;
-  const int32_t nrows = ntr + (sampling ? gb : 0);
-  const int64_t slot0 = (int64_t)b * P.spr;
-  const TempConst tc = temp_const(sampling ? T : 1.f);
-
-  // 1. Merge row partials: wavefront w takes rows w, w+4, ...; lane p holds slice p.
-  for (int32_t r0 = 0; r0 < nrows; r0 += kWaves * 4) {
-    Partial pv[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int32_t r = r0 + wave + kWaves * q;
-      pv[q].m = -INFINITY;
-      pv[q].idx = INT32_MAX;
-      pv[q].s = 0.0;
-      if (r < nrows && lane < P.nsplit) {
-        const int64_t slot = r < ntr ? slot0 + r : slot0 + P.gamma + 1 + (r - ntr);
-        pv[q] = P.parts[slot * P.nsplit + lane];
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int32_t r = r0 + wave + kWaves * q;
-      if (r >= nrows) break;  // uniform across the wavefront
-      const Partial *rowp = P.parts + (r < ntr ? slot0 + r : slot0 + P.gamma + 1 + (r - ntr)) * P.nsplit;
-      if (sampling) {
-        float m = pv[q].m;
-        for (int32_t p = lane + 64; p < P.nsplit; p += 64) m = fmaxf(m, rowp[p].m);
-        const float M = wave_max(m);
-        double f = pv[q].m != -INFINITY
-                       ? pv[q].s * exp2(((double)pv[q].m - (double)M) * tc.c)
-                       : 0.0;
-        for (int32_t p = lane + 64; p < P.nsplit; p += 64) {
-          const Partial o = rowp[p];
-          if (o.m != -INFINITY) f += o.s * exp2(((double)o.m - (double)M) * tc.c);
-        }
-        const double S = wave_sum(f);
-        if (lane == 0) {
-          s_m[r] = M;
-          s_s[r] = S;
-        }
-      } else {
-        float bv = pv[q].m;
-        int32_t bi = pv[q].idx;
-        for (int32_t p = lane + 64; p < P.nsplit; p += 64) argmax_merge(bv, bi, rowp[p].m, rowp[p].idx);
-        wave_argmax(bv, bi);
-        if (lane == 0) {
-          s_m[r] = bv;
-          s_i[r] = bi;
-        }
-      }
-    }
-  }
-  __syncthreads();
-
-  // 2. Accept tests (lane i = draft position i) and the first rejection; slice 0 writes.
-  if (wave == 0) {
-    bool accept = false;
-    double p = 0.0, q = 0.0;
-    if (lane < gb) {
-      const int32_t x = P.tokens[dbase + lane];
-      if (!sampling) {
-        accept = x == s_i[lane];
-      } else {
-        if (x >= 0 && x < P.V) {
-          const double zt = logit_at<DT>(P.target, (tbase + lane) * P.V + x);
-          const double zd = logit_at<DT>(P.draft, (dbase + lane) * P.V + x);
-          p = exp2((zt - (double)s_m[lane]) * tc.c) / s_s[lane];
-          q = exp2((zd - (double)s_m[ntr + lane]) * tc.c) / s_s[ntr + lane];
-        }
-        const double u = (double)P.uniforms[2 * (tbase + lane)];
-        accept = u * q < p;
-      }
-    }
-    const uint64_t acc_mask = __ballot(accept);
-    const uint64_t valid = gb >= 64 ? ~0ull : ((1ull << gb) - 1ull);
-    const uint64_t rej = ~acc_mask & valid;
-    const int32_t j = rej ? (int32_t)(__ffsll((long long)rej) - 1) : gb;
-    if (lane == 0) s_j = j;
-    if (split == 0) {
-      for (int32_t i = lane; i <= gb; i += 64) {
-        if (i != j) P.out_tokens[tbase + i] = i < j ? P.tokens[dbase + i] : -1;
-      }
-      if (lane == 0) {
-        P.out_n[b] = j;
-        Stop st = {};
-        st.j = j;
-        if (!sampling) {
-          P.out_tokens[tbase + j] = s_i[j];
-          st.mode = kModeNone;
-        } else {
-          st.mode = j < gb ? kModeResidual : kModeBonus;
-          st.mt = s_m[j];
-          st.st = s_s[j];
-          st.c_hi = tc.c_hi;
-          st.c_lo = tc.c_lo;
-          if (j < gb) {
-            st.md = s_m[ntr + j];
-            const double rho = s_s[j] / s_s[ntr + j];
-            st.rho_hi = (float)rho;
-            st.rho_lo = (float)(rho - (double)st.rho_hi);
-          }
-        }
-        P.stop[b] = st;
-      }
-      if (sampling && lane < gb) {
-        if (P.p_x) P.p_x[dbase + lane] = p;
-        if (P.q_x) P.q_x[dbase + lane] = q;
-      }
-    }
-  }
-  if (split == 0) {
-    for (int32_t r = tid; r < nrows; r += kThreads) {
-      if (r < ntr) {
-        if (P.row_max_t) P.row_max_t[tbase + r] = s_m[r];
-        if (sampling && P.row_sum_t) P.row_sum_t[tbase + r] = s_s[r];
-      } else {
-        if (P.row_max_d) P.row_max_d[dbase + r - ntr] = s_m[r];
-        if (P.row_sum_d) P.row_sum_d[dbase + r - ntr] = s_s[r];
-      }
-    }
-  }
-  __syncthreads();
-  if (!sampling) return;
-
-  // 3. This slice of the stop row(s): one fp64 sum per 64-unit chunk, chunks interleaved
-  //    across the wavefronts, NC chunks in flight per wavefront.
-  const int32_t j = s_j;
-  Stop st = {};
-  st.mode = j < gb ? kModeResidual : kModeBonus;
-  st.mt = s_m[j];
-  st.c_hi = tc.c_hi;
-  st.c_lo = tc.c_lo;
-  if (j < gb) {
-    st.md = s_m[ntr + j];
-    const double rho = s_s[j] / s_s[ntr + j];
-    st.rho_hi = (float)rho;
-    st.rho_lo = (float)(rho - (double)st.rho_hi);
-  }
-  const Store *tr = static_cast<const Store *>(row_ptr<DT>(P.target, tbase + j, P.V));
-  const Store *dr = static_cast<const Store *>(row_ptr<DT>(P.draft, dbase + j, P.V));
-  const int64_t nunits = (P.V + W - 1) / W;
-  const int64_t nchunks = (nunits + 63) / 64;
-  const int64_t per = (nchunks + P.nsplit_r - 1) / P.nsplit_r;
-  const int64_t c_lo = (int64_t)split * per;
-  const int64_t c_hi = c_lo + per < nchunks ? c_lo + per : nchunks;
-  double *cs = P.chunk_sums + (int64_t)b * P.chunk_stride;
-  for (int64_t c0 = c_lo + wave; c0 < c_hi; c0 += (int64_t)kWaves * NC) {
-    typename U::Raw rt[NC], rd[NC];
-#pragma unroll
-    for (int q = 0; q < NC; ++q) {
-      const int64_t c = c0 + (int64_t)q * kWaves;
-      const int64_t u = c * 64 + lane;
-      const bool ok = c < c_hi && u < nunits;
-      rt[q] = ok ? U::template load<false>(tr, u) : U::filler();
-      rd[q] = ok && st.mode == kModeResidual ? U::template load<false>(dr, u) : U::filler();
-    }
-#pragma unroll
-    for (int q = 0; q < NC; ++q) {
-      const int64_t c = c0 + (int64_t)q * kWaves;
-      if (c >= c_hi) break;  // uniform across the wavefront
-      float zt[W], zd[W], r[W];
-      U::cvt(rt[q], zt);
-      U::cvt(rd[q], zd);
-      resid_weights<W>(zt, zd, st, r);
-      const float us = unit_sum<W>(r);
-      const double s = wave_sum(c * 64 + lane < nunits ? (double)us : 0.0);
-      if (lane == 0) cs[c] = s;
-    }
-  }
-}
-
-// ------------------------------------------------------------------ k_draw
 
 // Weights and pairwise sum of unit u of the stop row(s).
 template <int DT, bool VEC>
@@ -711,20 +578,21 @@ __device__ __forceinline__ float resid_unit(const typename Unit<DT, VEC>::Store 
 }
 
 // Draw from p over a whole target row (used only when the residual is empty after rounding).
-template <int DT>
+template <int DT, int NT>
 __device__ int32_t draw_from_row(const void *tr, int64_t V, const Stop &st, double u,
                                  double *shd, int32_t *shi, double &total) {
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
-  const int64_t per = (V + kThreads - 1) / kThreads;
+  const int64_t per = (V + NT - 1) / NT;
   const int64_t a = tid * per;
   const int64_t e_ = a + per < V ? a + per : V;
   double mine = 0.0;
   for (int64_t k = a; k < e_; ++k)
     mine += (double)ex2(arg_shifted(logit_at<DT>(tr, k), st.mt, st.c_hi, st.c_lo));
-  const double before = block_excl_scan(mine, shd, total);
+  const double before = block_excl_scan<NW>(mine, shd, total);
   const double target = u * total;
-  const int32_t first = block_first(mine > 0.0 && before + mine > target, shi);
-  const int32_t last = block_last(mine > 0.0, shi);
+  const int32_t first = block_first<NW>(mine > 0.0 && before + mine > target, shi);
+  const int32_t last = block_last<NW>(mine > 0.0, shi);
   const int32_t pick = first != INT32_MAX ? first : last;
   int32_t tok = -1;
   if (tid == pick) {
@@ -746,47 +614,241 @@ __device__ int32_t draw_from_row(const void *tr, int64_t V, const Stop &st, doub
   return tok;
 }
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_draw(Params P) {
+// Merged rows of one request, in LDS.
+struct ReqLds {
+  float m[2 * SPEC_MAX_GAMMA + 1];   // row maxima: target rows 0..gb, then draft rows
+  double s[2 * SPEC_MAX_GAMMA + 1];  // row sums (sampled requests)
+  int32_t i[SPEC_MAX_GAMMA + 1];     // target argmax (greedy requests)
+  int32_t j;                         // the stop row
+};
+
+// Steps 1 and 2 of finishing request b, for a workgroup of NT threads:
+//  1. merge the row partials (one wavefront per row, one lane per slice, fp64);
+//  2. accept tests lane-parallel on wavefront 0 (p(x), q(x) in fp64 from the logits that
+//     k_rowstats captured) and the first rejection by ballot + find-first-set.
+// With `write`, the outputs and the row probes are written.  Ends with a barrier; the stop
+// row is in L.j.  Returns the request's temperature constant.
+template <int NT>
+__device__ TempConst finish_head(const Params &P, int32_t b, bool write, ReqLds &L,
+                                 int64_t &dbase, int32_t &gb, bool &sampling) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float T;
+  request(P, b, dbase, gb, T);
+  sampling = T > 0.f;
+  const int64_t tbase = dbase + b;
+  const int32_t ntr = gb + 1;
+  const int32_t nrows = ntr + (sampling ? gb : 0);
+  const int64_t slot0 = (int64_t)b * P.spr;
+  const TempConst tc = temp_const(sampling ? T : 1.f);
+
+  // What the accept tests read besides the merged rows goes out first: lane i of wavefront 0
+  // loads draft i's token, its uniform, and the two logits at the token.
+  int32_t x = -1;
+  float ux = 0.f, zt = 0.f, zd = 0.f;
+  if (wave == 0 && lane < gb) {
+    x = P.tokens[dbase + lane];
+    if (sampling) {
+      ux = P.uniforms[2 * (tbase + lane)];
+      zt = P.gz[slot0 + lane];
+      zd = P.gz[slot0 + P.gamma + 1 + lane];
+    }
+  }
+
+  // 1. Wavefront w takes rows w, w + NW, ...; lane p holds slice p.
+  for (int32_t r0 = 0; r0 < nrows; r0 += NW * 4) {
+    Partial pv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int32_t r = r0 + wave + NW * q;
+      pv[q].m = -INFINITY;
+      pv[q].idx = INT32_MAX;
+      pv[q].s = 0.0;
+      if (r < nrows && lane < P.nsplit) {
+        const int64_t slot = r < ntr ? slot0 + r : slot0 + P.gamma + 1 + (r - ntr);
+        pv[q] = P.parts[slot * P.nsplit + lane];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int32_t r = r0 + wave + NW * q;
+      if (r >= nrows) break;  // uniform across the wavefront
+      const Partial *rowp = P.parts + (r < ntr ? slot0 + r : slot0 + P.gamma + 1 + (r - ntr)) * P.nsplit;
+      if (sampling) {
+        float m = pv[q].m;
+        for (int32_t p = lane + 64; p < P.nsplit; p += 64) m = fmaxf(m, rowp[p].m);
+        const float M = wave_max(m);
+        double f = pv[q].m != -INFINITY
+                       ? pv[q].s * exp2(((double)pv[q].m - (double)M) * tc.c)
+                       : 0.0;
+        for (int32_t p = lane + 64; p < P.nsplit; p += 64) {
+          const Partial o = rowp[p];
+          if (o.m != -INFINITY) f += o.s * exp2(((double)o.m - (double)M) * tc.c);
+        }
+        const double S = wave_sum(f);
+        if (lane == 0) {
+          L.m[r] = M;
+          L.s[r] = S;
+        }
+      } else {
+        float bv = pv[q].m;
+        int32_t bi = pv[q].idx;
+        for (int32_t p = lane + 64; p < P.nsplit; p += 64) argmax_merge(bv, bi, rowp[p].m, rowp[p].idx);
+        wave_argmax(bv, bi);
+        if (lane == 0) {
+          L.m[r] = bv;
+          L.i[r] = bi;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // 2. Lane i = draft position i.
+  if (wave == 0) {
+    bool accept = false;
+    double p = 0.0, q = 0.0;
+    if (lane < gb) {
+      if (!sampling) {
+        accept = x == L.i[lane];
+      } else {
+        if (x >= 0 && x < P.V) {
+          p = exp2(((double)zt - (double)L.m[lane]) * tc.c) / L.s[lane];
+          q = exp2(((double)zd - (double)L.m[ntr + lane]) * tc.c) / L.s[ntr + lane];
+        }
+        accept = (double)ux * q < p;
+      }
+    }
+    const uint64_t acc_mask = __ballot(accept);
+    const uint64_t valid = gb >= 64 ? ~0ull : ((1ull << gb) - 1ull);
+    const uint64_t rej = ~acc_mask & valid;
+    const int32_t j = rej ? (int32_t)(__ffsll((long long)rej) - 1) : gb;
+    if (lane == 0) L.j = j;
+    if (write) {
+      if (lane < gb && lane != j) P.out_tokens[tbase + lane] = lane < j ? x : -1;
+      if (lane == 0) {
+        if (j < gb) P.out_tokens[tbase + gb] = -1;
+        if (!sampling) P.out_tokens[tbase + j] = L.i[j];
+        P.out_n[b] = j;
+      }
+      if (sampling && lane < gb) {
+        if (P.p_x) P.p_x[dbase + lane] = p;
+        if (P.q_x) P.q_x[dbase + lane] = q;
+      }
+    }
+  }
+  if (write) {
+    for (int32_t r = tid; r < nrows; r += NT) {
+      if (r < ntr) {
+        if (P.row_max_t) P.row_max_t[tbase + r] = L.m[r];
+        if (sampling && P.row_sum_t) P.row_sum_t[tbase + r] = L.s[r];
+      } else {
+        if (P.row_max_d) P.row_max_d[dbase + r - ntr] = L.m[r];
+        if (P.row_sum_d) P.row_sum_d[dbase + r - ntr] = L.s[r];
+      }
+    }
+  }
+  __syncthreads();
+  return tc;
+}
+
+// The residual weights' constants for stop row j of a sampled request.
+__device__ __forceinline__ Stop make_stop(const ReqLds &L, int32_t gb, const TempConst &tc,
+                                          int64_t trow, int64_t drow) {
+  const int32_t j = L.j, ntr = gb + 1;
+  Stop st = {};
+  st.mode = j < gb ? kModeResidual : kModeBonus;
+  st.mt = L.m[j];
+  st.st = L.s[j];
+  st.c_hi = tc.c_hi;
+  st.c_lo = tc.c_lo;
+  if (j < gb) {
+    st.md = L.m[ntr + j];
+    const double rho = L.s[j] / L.s[ntr + j];
+    st.rho_hi = (float)rho;
+    st.rho_lo = (float)(rho - (double)st.rho_hi);
+  }
+  st.trow = trow;
+  st.drow = drow;
+  return st;
+}
+
+// Step 3: units [ub, ub_end) of the stop row(s), NT * RU units per pass with all loads of a
+// pass in flight; one fp64 sum per 64-unit chunk (one wavefront-wide load) into cs.
+template <int DT, bool VEC, int NT, int RU>
+__device__ __forceinline__ void stream_chunks(const Params &P, const Stop &st, int64_t ub,
+                                              int64_t ub_end, double *cs) {
   using U = Unit<DT, VEC>;
   using Store = typename U::Store;
   constexpr int W = U::W;
-  __shared__ int32_t s_c, s_tok;
-  __shared__ double s_local;
-  __shared__ double shd[kWaves];
-  __shared__ int32_t shi[kWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int32_t b = blockIdx.x;
-  const Stop st = P.stop[b];
-  if (st.mode == kModeNone) return;
-  int64_t dbase;
-  int32_t gb;
-  float T;
-  request(P, b, dbase, gb, T);
-  const int64_t tbase = dbase + b;
-  const int32_t j = st.j;
-  const Store *tr = static_cast<const Store *>(row_ptr<DT>(P.target, tbase + j, P.V));
-  const Store *dr = static_cast<const Store *>(row_ptr<DT>(P.draft, dbase + j, P.V));
-  const double u = (double)P.uniforms[2 * (tbase + j) + 1];
+  const Store *tr = static_cast<const Store *>(row_ptr<DT>(P.target, st.trow, P.V));
+  const Store *dr = static_cast<const Store *>(row_ptr<DT>(P.draft, st.drow, P.V));
+  const bool resid = st.mode == kModeResidual;
+  for (; ub < ub_end; ub += (int64_t)NT * RU) {
+    typename U::Raw rt[RU], rd[RU];
+#pragma unroll
+    for (int q = 0; q < RU; ++q) {
+      const int64_t u = ub + q * NT + tid;
+      rt[q] = u < ub_end ? U::template load<false>(tr, u) : U::filler();
+      rd[q] = resid && u < ub_end ? U::template load<false>(dr, u) : U::filler();
+    }
+#pragma unroll
+    for (int q = 0; q < RU; ++q) {
+      const int64_t c0 = ub + q * NT + wave * 64;  // first unit of this chunk
+      if (c0 >= ub_end) break;  // uniform across the wavefront
+      float zt[W], zd[W], r[W];
+      U::cvt(rt[q], zt);
+      U::cvt(rd[q], zd);
+      resid_weights<W>(zt, zd, st, r);
+      const float us = unit_sum<W>(r);
+      const double sum = wave_sum(c0 + lane < ub_end ? (double)us : 0.0);
+      if (lane == 0) cs[c0 / 64] = sum;
+    }
+  }
+}
+
+// LDS of the draw.
+template <int NW>
+struct DrawLds {
+  double shd[NW];
+  int32_t shi[NW];
+  int32_t c, tok;
+  double local;
+};
+
+// Step 4, the draw, by a workgroup of NT threads once every chunk sum of request b is in cs:
+// a block scan over the chunk sums picks the chunk holding u * R, a wavefront scan over its
+// 64 units picks the unit, and a walk over the unit's elements gives the token.
+template <int DT, bool VEC, int NT>
+__device__ void draw_token(const Params &P, int32_t b, const Stop &st, const double *cs,
+                           DrawLds<NT / 64> &D) {
+  using U = Unit<DT, VEC>;
+  using Store = typename U::Store;
+  constexpr int W = U::W;
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const Store *tr = static_cast<const Store *>(row_ptr<DT>(P.target, st.trow, P.V));
+  const Store *dr = static_cast<const Store *>(row_ptr<DT>(P.draft, st.drow, P.V));
+  const double u = (double)P.uniforms[2 * st.trow + 1];
   const int64_t nunits = (P.V + W - 1) / W;
   const int64_t nchunks = (nunits + 63) / 64;
-  const double *cs = P.chunk_sums + (int64_t)b * P.chunk_stride;
 
-  // Chunk holding u * R: each thread sums a contiguous run of chunks, a block scan places
-  // the runs, and the thread whose run crosses the target walks it.
-  const int64_t per = (nchunks + kThreads - 1) / kThreads;
+  // Each thread sums a contiguous run of chunks, a block scan places the runs, and the
+  // thread whose run crosses the target walks it.
+  const int64_t per = (nchunks + NT - 1) / NT;
   const int64_t a = tid * per;
   const int64_t e_ = a + per < nchunks ? a + per : nchunks;
   double mine = 0.0;
   for (int64_t c = a; c < e_; ++c) mine += cs[c];
   double R;
-  const double before = block_excl_scan(mine, shd, R);
+  const double before = block_excl_scan<NW>(mine, D.shd, R);
   const double target = u * R;
-  const int32_t first = block_first(mine > 0.0 && before + mine > target, shi);
-  const int32_t lastt = block_last(mine > 0.0, shi);
+  const int32_t first = block_first<NW>(mine > 0.0 && before + mine > target, D.shi);
+  const int32_t lastt = block_last<NW>(mine > 0.0, D.shi);
   if (tid == 0) {
-    s_c = -1;
-    s_tok = -1;
+    D.c = -1;
+    D.tok = -1;
   }
   __syncthreads();
   const int32_t pick = first != INT32_MAX ? first : lastt;
@@ -798,20 +860,20 @@ __global__ __launch_bounds__(kThreads) void k_draw(Params P) {
       if (v > 0.0) {
         lastpos = c;
         if (first != INT32_MAX && run + v > target) {
-          s_c = (int32_t)c;
-          s_local = target - run;
+          D.c = (int32_t)c;
+          D.local = target - run;
           break;
         }
       }
       run += v;
     }
-    if (s_c < 0) {
-      s_c = (int32_t)lastpos;
-      s_local = INFINITY;
+    if (D.c < 0) {
+      D.c = (int32_t)lastpos;
+      D.local = INFINITY;
     }
   }
   __syncthreads();
-  const int32_t csel = s_c;
+  const int32_t csel = D.c;
   if (csel >= 0) {
     if (wave == 0) {
       // The chunk's 64 units: a wavefront scan picks the unit, its lane walks the elements.
@@ -820,7 +882,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(Params P) {
       float r[W];
       float us = 0.f;
       if (uu < nunits) us = resid_unit<DT, VEC>(tr, dr, uu, st, r);
-      const double local = s_local;
+      const double local = D.local;
       const double incl = wave_incl_scan((double)us);
       const uint64_t cross = __ballot(us > 0.f && incl > local);
       const uint64_t pos = __ballot(us > 0.f);
@@ -836,12 +898,12 @@ __global__ __launch_bounds__(kThreads) void k_draw(Params P) {
             if (cross && tok < 0 && run > local) tok = lastpos;
           }
         }
-        s_tok = tok >= 0 ? tok : lastpos;
+        D.tok = tok >= 0 ? tok : lastpos;
       }
     }
     __syncthreads();
     if (tid == 0) {
-      P.out_tokens[tbase + j] = s_tok;
+      P.out_tokens[st.trow] = D.tok;
       if (P.resid_mass) P.resid_mass[b] = R / st.st;
     }
   } else {
@@ -849,22 +911,88 @@ __global__ __launch_bounds__(kThreads) void k_draw(Params P) {
     Stop sp = st;
     sp.mode = kModeBonus;
     double tot;
-    const int32_t tok = draw_from_row<DT>(tr, P.V, sp, u, shd, shi, tot);
-    if (tok >= 0) s_tok = tok;
+    const int32_t tok = draw_from_row<DT, NT>(tr, P.V, sp, u, D.shd, D.shi, tot);
+    if (tok >= 0) D.tok = tok;
     __syncthreads();
     if (tid == 0) {
-      P.out_tokens[tbase + j] = s_tok;
+      P.out_tokens[st.trow] = D.tok;
       if (P.resid_mass) P.resid_mass[b] = tot / st.st;
     }
   }
 }
 
+// ------------------------------------------------------------------ k_finish (fused path)
+
+// One workgroup of NT threads per request does all of steps 1-4; the chunk sums it writes are
+// read back by the same workgroup after a barrier.  Used when one workgroup can stream a stop
+// row pair about as fast as the whole GPU could share it out, counting the two launches the
+// split path adds.
+template <int DT, bool VEC, int NT>
+__global__ __launch_bounds__(NT) void k_finish(Params P) {
+  constexpr int W = Unit<DT, VEC>::W;
+  __shared__ ReqLds L;
+  __shared__ DrawLds<NT / 64> D;
+  const int32_t b = (int32_t)blockIdx.x;
+  int64_t dbase;
+  int32_t gb;
+  bool sampling;
+  const TempConst tc = finish_head<NT>(P, b, true, L, dbase, gb, sampling);
+  if (!sampling) return;
+  const Stop st = make_stop(L, gb, tc, dbase + b + L.j, dbase + L.j);
+  double *cs = P.chunk_sums + (int64_t)b * P.chunk_stride;
+  stream_chunks<DT, VEC, NT, kFinPassUnits / NT>(P, st, 0, (P.V + W - 1) / W, cs);
+  __syncthreads();  // the chunk sums are read below by other wavefronts of this workgroup
+  draw_token<DT, VEC, NT>(P, b, st, cs, D);
+}
+
+// ------------------------------------------------------------------ split path
+
+// k_resid: workgroups (request, slice of kResSliceUnits units of the stop row).  Every
+// workgroup of a request repeats steps 1-2 (cheap next to the stream, and it saves a launch);
+// slice 0 writes the outputs and the stop record for k_draw.  Sampled requests then stream
+// their slice (step 3).
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_resid(Params P) {
+  constexpr int W = Unit<DT, VEC>::W;
+  __shared__ ReqLds L;
+  const int32_t b = (int32_t)(blockIdx.x / P.nsplit_r);
+  const int32_t split = (int32_t)(blockIdx.x % P.nsplit_r);
+  int64_t dbase;
+  int32_t gb;
+  bool sampling;
+  const TempConst tc = finish_head<kThreads>(P, b, split == 0, L, dbase, gb, sampling);
+  if (!sampling) return;
+  const Stop st = make_stop(L, gb, tc, dbase + b + L.j, dbase + L.j);
+  if (split == 0 && threadIdx.x == 0) P.stop[b] = st;
+  const int64_t nunits = (P.V + W - 1) / W;
+  const int64_t ub = (int64_t)split * kResSliceUnits;
+  const int64_t ue = ub + kResSliceUnits < nunits ? ub + kResSliceUnits : nunits;
+  stream_chunks<DT, VEC, kThreads, kResSliceUnits / kThreads>(P, st, ub, ue,
+                                                              P.chunk_sums + (int64_t)b * P.chunk_stride);
+}
+
+// k_draw: one workgroup per request, step 4 from k_resid's stop record and chunk sums.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_draw(Params P) {
+  __shared__ DrawLds<kWaves> D;
+  const int32_t b = (int32_t)blockIdx.x;
+  int64_t dbase;
+  int32_t gb;
+  float T;
+  request(P, b, dbase, gb, T);
+  if (!(T > 0.f)) return;
+  const Stop st = P.stop[b];
+  draw_token<DT, VEC, kThreads>(P, b, st, P.chunk_sums + (int64_t)b * P.chunk_stride, D);
+}
+
 // ------------------------------------------------------------------ host side
 
 struct Plan {
-  int32_t spr, nsplit, nsplit_r;
+  int32_t spr, nsplit;
   int64_t split_len, chunk_stride;
-  size_t off_parts, off_stop, off_chunks, total;
+  bool fused;               // finishing path: k_finish, or k_resid + k_draw
+  int32_t fin_threads;      // k_finish workgroup size
+  size_t off_parts, off_gz, off_stop, off_chunks, total;
 };
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -889,16 +1017,18 @@ bool make_plan(int32_t B, int32_t gamma, int64_t V, int dtype, bool greedy, Plan
   }
   pl.nsplit = (int32_t)ceil_div(V, len);  // no empty slice
   pl.split_len = len;
-  // k_resid: enough workgroups per request to spread the stop rows over the GPU.
-  pl.chunk_stride = ceil_div(V, 64);       // chunks per row on the element path (the most)
-  const int64_t vec_chunks = ceil_div(ceil_div(V, dtype == SPEC_F32 ? 4 : 8), 64);
-  int64_t nsr = ceil_div(kResidGrid, bb);
-  if (nsr > vec_chunks) nsr = vec_chunks;
-  if (nsr < 1) nsr = 1;
-  pl.nsplit_r = greedy ? 1 : (int32_t)nsr;
+  // Finishing path.  One workgroup streams a request's stop row pair at about what one CU
+  // draws (~25 GB/s on MI355X); the split path shares all stop rows out over the GPU
+  // (~6 TB/s) but adds two launches (~8 us).  Greedy requests stream nothing.
+  const double pair = 2.0 * (double)V * (dtype == SPEC_F32 ? 4 : 2);
+  pl.fused = greedy || pair / 25e9 <= (double)bb * pair / 6e12 + 8e-6;
+  pl.fin_threads = bb > 256 ? 512 : 1024;
+  // Chunk sums of the stop rows; the element path (one element per unit) has the most chunks.
+  pl.chunk_stride = ceil_div(V, 64);
   pl.off_parts = 0;
-  pl.off_stop = align_up((size_t)bb * pl.spr * pl.nsplit * sizeof(Partial));
-  pl.off_chunks = pl.off_stop + align_up((size_t)bb * sizeof(Stop));
+  pl.off_gz = align_up((size_t)bb * pl.spr * pl.nsplit * sizeof(Partial));
+  pl.off_stop = pl.off_gz + (greedy ? 0 : align_up((size_t)bb * pl.spr * sizeof(float)));
+  pl.off_chunks = pl.off_stop + (pl.fused ? 0 : align_up((size_t)bb * sizeof(Stop)));
   pl.total = pl.off_chunks + (greedy ? 0 : align_up((size_t)bb * pl.chunk_stride * sizeof(double)));
   return true;
 }
@@ -918,21 +1048,28 @@ int record(const spec_probe *probe, int k, hipStream_t s) {
 int launched() { return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP; }
 
 template <int DT, bool VEC>
-int run(const Params &P, const Plan &pl, const spec_probe *probe, hipStream_t s, bool greedy) {
+int run(Params P, const Plan &pl, const spec_probe *probe, hipStream_t s) {
   const int64_t slots = (int64_t)P.B * pl.spr;
   const uint32_t gy = (uint32_t)(slots < kMaxGridY ? slots : kMaxGridY);
   const uint32_t gz = (uint32_t)ceil_div(slots, gy);
+  const dim3 grid_b((uint32_t)P.B);
   SPEC_TRY(record(probe, 0, s));
   k_rowstats<DT, VEC><<<dim3((uint32_t)pl.nsplit, gy, gz), dim3(kThreads), 0, s>>>(P);
   SPEC_TRY(launched());
   SPEC_TRY(record(probe, 1, s));
   SPEC_TRY(record(probe, 2, s));
-  k_resid<DT, VEC><<<dim3((uint32_t)((int64_t)P.B * pl.nsplit_r)), dim3(kThreads), 0, s>>>(P);
-  SPEC_TRY(launched());
-  SPEC_TRY(record(probe, 3, s));
-  if (!greedy) {
+  if (pl.fused) {
+    if (pl.fin_threads == 512) k_finish<DT, VEC, 512><<<grid_b, dim3(512), 0, s>>>(P);
+    else k_finish<DT, VEC, 1024><<<grid_b, dim3(1024), 0, s>>>(P);
+    SPEC_TRY(launched());
+    SPEC_TRY(record(probe, 3, s));
+  } else {
+    P.nsplit_r = (int32_t)ceil_div(ceil_div(P.V, Unit<DT, VEC>::W), kResSliceUnits);
+    k_resid<DT, VEC><<<dim3((uint32_t)((int64_t)P.B * P.nsplit_r)), dim3(kThreads), 0, s>>>(P);
+    SPEC_TRY(launched());
+    SPEC_TRY(record(probe, 3, s));
     SPEC_TRY(record(probe, 4, s));
-    k_draw<DT, VEC><<<dim3((uint32_t)P.B), dim3(kThreads), 0, s>>>(P);
+    k_draw<DT, VEC><<<grid_b, dim3(kThreads), 0, s>>>(P);
     SPEC_TRY(launched());
     SPEC_TRY(record(probe, 5, s));
   }
@@ -951,23 +1088,25 @@ int setup(Params &P, const Plan &pl, void *workspace, size_t workspace_bytes) {
   if (!workspace) return SPEC_ERR_NULL;
   if (((uintptr_t)workspace & (kAlign - 1)) != 0 || workspace_bytes < pl.total)
     return SPEC_ERR_WORKSPACE;
-  if ((int64_t)P.B * pl.nsplit_r > (int64_t)UINT32_MAX) return SPEC_ERR_SHAPE;
+  if ((int64_t)P.B * pl.spr > kMaxGridY * kMaxGridY) return SPEC_ERR_SHAPE;
   char *ws = static_cast<char *>(workspace);
   P.parts = reinterpret_cast<Partial *>(ws + pl.off_parts);
+  P.gz = reinterpret_cast<float *>(ws + pl.off_gz);
   P.stop = reinterpret_cast<Stop *>(ws + pl.off_stop);
+  // the split path's grid, for the widest case (one element per unit)
+  if (!pl.fused && (int64_t)P.B * ceil_div(P.V, kResSliceUnits) > (int64_t)UINT32_MAX)
+    return SPEC_ERR_SHAPE;
   P.chunk_sums = reinterpret_cast<double *>(ws + pl.off_chunks);
   P.chunk_stride = pl.chunk_stride;
   P.spr = pl.spr;
   P.nsplit = pl.nsplit;
   P.split_len = pl.split_len;
-  P.nsplit_r = pl.nsplit_r;
   return SPEC_OK;
 }
 
 template <int DT>
-int dispatch(const Params &P, const Plan &pl, const spec_probe *probe, hipStream_t s, bool vec,
-             bool greedy) {
-  return vec ? run<DT, true>(P, pl, probe, s, greedy) : run<DT, false>(P, pl, probe, s, greedy);
+int dispatch(const Params &P, const Plan &pl, const spec_probe *probe, hipStream_t s, bool vec) {
+  return vec ? run<DT, true>(P, pl, probe, s) : run<DT, false>(P, pl, probe, s);
 }
 
 }  // namespace
@@ -1033,8 +1172,8 @@ int spec_verify_sample(const void *target_logits, const void *draft_logits, int 
   const int es = dtype == SPEC_F32 ? 4 : 2;
   const bool vec = aligned16(target_logits) && aligned16(draft_logits) && (V * es) % 16 == 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return dtype == SPEC_F32 ? dispatch<SPEC_F32>(P, pl, probe, s, vec, false)
-                           : dispatch<SPEC_BF16>(P, pl, probe, s, vec, false);
+  return dtype == SPEC_F32 ? dispatch<SPEC_F32>(P, pl, probe, s, vec)
+                           : dispatch<SPEC_BF16>(P, pl, probe, s, vec);
 }
 
 int spec_verify_greedy(const void *target_logits, int dtype, const int32_t *draft_tokens,
@@ -1062,8 +1201,8 @@ int spec_verify_greedy(const void *target_logits, int dtype, const int32_t *draf
   const int es = dtype == SPEC_F32 ? 4 : 2;
   const bool vec = aligned16(target_logits) && (V * es) % 16 == 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return dtype == SPEC_F32 ? dispatch<SPEC_F32>(P, pl, probe, s, vec, true)
-                           : dispatch<SPEC_BF16>(P, pl, probe, s, vec, true);
+  return dtype == SPEC_F32 ? dispatch<SPEC_F32>(P, pl, probe, s, vec)
+                           : dispatch<SPEC_BF16>(P, pl, probe, s, vec);
 }
 
 }  // extern "C"

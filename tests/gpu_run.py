@@ -11,6 +11,43 @@ def to_device(w, device="cuda"):
     return workloads.to_torch(w, device)
 
 
+def launches(w, *, greedy: bool = False) -> int:
+    """Kernel launches one call makes on workload ``w``, read from the probe's event slots
+    (the library records events 2k / 2k+1 around its k-th launch)."""
+    import ctypes
+    import torch
+    hip = ctypes.CDLL("libamdhip64.so")
+    evs = []
+    for _ in range(8):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    d = to_device(w)
+    code = sv.SPEC_F32 if w.dtype == "f32" else sv.SPEC_BF16
+    ws = sv.alloc_workspace(w.B, w.gamma, w.V, code)
+    out = torch.empty(w.R_t, dtype=torch.int32, device="cuda")
+    nacc = torch.empty(w.B, dtype=torch.int32, device="cuda")
+    pr = sv.make_probe(events=evs)
+    if greedy:
+        sv.spec_verify_greedy(d["target"], d["tokens"], w.gamma, out, nacc, ws,
+                              cu_draft=d["cu"], probe=pr)
+    else:
+        sv.spec_verify_sample(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temps"],
+                              w.gamma, out, nacc, ws, cu_draft=d["cu"], probe=pr)
+    torch.cuda.synchronize()
+    n = 0
+    ms = ctypes.c_float()
+    for k in range(4):
+        if hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(evs[2 * k]),
+                                   ctypes.c_void_p(evs[2 * k + 1])) != 0:
+            hip.hipGetLastError()  # events never recorded: clear the error the query left
+            break
+        n += 1
+    for e in evs:
+        hip.hipEventDestroy(ctypes.c_void_p(e))
+    return n
+
+
 def run(w, *, greedy: bool = False, probe: bool = True, dev=None, workspace=None,
         sync: bool = True) -> dict:
     """Verify workload ``w`` on the GPU; returns numpy outputs (and probe arrays)."""

@@ -10,7 +10,7 @@ import pytest
 import oracle
 import workloads
 from tests import parity
-from tests.gpu_run import run, to_device
+from tests.gpu_run import launches, run, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -74,6 +74,24 @@ def test_long_rows_with_multi_tile_slices():
     w = workloads.small(B=2, gamma=3, V=600_000, dtype="f32", seed=32,
                         temperatures=np.array([1.1, 0.5]), draft_sigma=0.6)
     _both(w)
+
+
+@pytest.mark.parametrize("B,gamma,V,dtype,launch_count", [
+    (300, 2, 4096, "bf16", 2),      # many requests, short rows: one workgroup per request
+    (5, 3, 16, "f32", 2),
+    (2, 3, 300_000, "bf16", 3),     # few requests, long rows: stop rows shared out
+    (3, 2, 250_001, "f32", 3),      # ... on the element path
+])
+def test_both_finishing_paths(B, gamma, V, dtype, launch_count):
+    # the library finishes requests either in one launch per request (k_finish) or in two
+    # (k_resid over slices of the stop rows, then k_draw); both must match the oracle
+    temps = np.where(np.arange(B) % 4 == 1, 0.0, np.linspace(0.4, 1.4, B))
+    w = workloads.small(B=B, gamma=gamma, V=V, dtype=dtype, seed=B * 7 + V, ragged=True,
+                        temperatures=temps, draft_sigma=0.9)
+    assert launches(w) == launch_count
+    _both(w)
+    assert launches(w, greedy=True) == 2
+    _both(w, greedy=True)
 
 
 # ----------------------------------------------------------------------- edge cases
@@ -176,10 +194,11 @@ def test_unaligned_rows_take_the_element_path():
     parity.compare(w, g, o)
 
 
-def test_bonus_fallback_when_residual_is_empty():
+@pytest.mark.parametrize("V", [256, 200_000])
+def test_bonus_fallback_when_residual_is_empty(V):
     # p = q at a rejected position (uniform at its upper edge): the residual is empty and
-    # the draw falls back to p, as the oracle does.
-    w = workloads.small(B=3, gamma=2, V=256, dtype="f32", seed=13, temperatures=1.0)
+    # the draw falls back to p, as the oracle does (both finishing paths).
+    w = workloads.small(B=3, gamma=2, V=V, dtype="f32", seed=13, temperatures=1.0)
     w.draft[:] = w.target[np.concatenate([[0, 1], [3, 4], [6, 7]])]
     w.uniforms[:, 0] = 1.0
     g, o, _ = _both(w)
