@@ -68,7 +68,7 @@ enum {
   SPEC_ERR_DTYPE = -3,      /* dtype is not a spec_dtype                                 */
   SPEC_ERR_WORKSPACE = -4,  /* workspace smaller than spec_verify_workspace_size, or not
                                256-byte aligned                                          */
-  SPEC_ERR_HIP = -5         /* a kernel launch or event record failed                    */
+  SPEC_ERR_HIP = -5         /* a kernel launch failed                                    */
 };
 
 /* Largest gamma (drafts per request) the kernels take. */
@@ -88,11 +88,10 @@ typedef struct spec_probe {
   double *resid_mass; /* [B] total probability mass of the distribution drawn from at the
                          stop row: sum_k max(p_k - q_k, 0) after a rejection, sum_k p_k
                          (= 1) for the bonus; sampled requests                            */
-  void *events[8];    /* host: hipEvent_t or NULL; events[2k] / events[2k+1] are recorded on
-                         `stream` just before / after the k-th kernel launch of the call
-                         (launch 0: row statistics; then either launch 1: accept tests,
-                         residual and draw in one, or launch 1: accept tests and residual,
-                         launch 2: draw); entries past the last launch are not touched  */
+  void *events[8];    /* host: hipEvent_t or NULL; events[2k] / events[2k+1] are recorded by
+                         the dispatch of the call's k-th kernel as it starts / ends (launch 0:
+                         row statistics, launch 1: accept tests, residual and draw); the
+                         entries for k = 2, 3 are not touched                             */
 } spec_probe;
 
 /*

@@ -127,20 +127,15 @@ def _check(rc: int, where: str):
         raise SpecVerifyError(rc, where)
 
 
-def spec_verify_sample(target_logits, draft_logits, draft_tokens, uniforms, temperatures,
-                       gamma: int, out_tokens, out_num_accepted, workspace,
-                       cu_draft=None, probe: Optional[_Probe] = None, stream=None) -> None:
-    """Asynchronous on the current (or given) stream.  ``target_logits [R_t, V]`` and
-    ``draft_logits [R_d, V]`` share one dtype (float32 / bfloat16); ``B`` is
-    ``temperatures.numel()``; ``workspace`` is a uint8 tensor of at least
-    ``spec_verify_workspace_size`` bytes."""
+def _sample_args(target_logits, draft_logits, draft_tokens, uniforms, temperatures, gamma,
+                 out_tokens, out_num_accepted, workspace, cu_draft, probe, stream):
     torch = _torch()
     B = temperatures.numel()
     V = target_logits.shape[-1]
     dt = dtype_code(target_logits)
     if draft_logits.dtype != target_logits.dtype:
         raise ValueError("target and draft logits must share a dtype")
-    rc = lib().spec_verify_sample(
+    return (
         _dev(target_logits, "target_logits"), _dev(draft_logits, "draft_logits"), dt,
         _dev(draft_tokens, "draft_tokens", torch.int32),
         _dev(uniforms, "uniforms", torch.float32),
@@ -150,17 +145,14 @@ def spec_verify_sample(target_logits, draft_logits, draft_tokens, uniforms, temp
         _dev(out_num_accepted, "out_num_accepted", torch.int32, B),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         None if probe is None else ctypes.byref(probe), _stream(stream))
-    _check(rc, "spec_verify_sample")
 
 
-def spec_verify_greedy(target_logits, draft_tokens, gamma: int, out_tokens,
-                       out_num_accepted, workspace, cu_draft=None,
-                       probe: Optional[_Probe] = None, stream=None) -> None:
-    """Temperature-zero verification; ``B`` is ``out_num_accepted.numel()``."""
+def _greedy_args(target_logits, draft_tokens, gamma, out_tokens, out_num_accepted, workspace,
+                 cu_draft, probe, stream):
     torch = _torch()
     B = out_num_accepted.numel()
     V = target_logits.shape[-1]
-    rc = lib().spec_verify_greedy(
+    return (
         _dev(target_logits, "target_logits"), dtype_code(target_logits),
         _dev(draft_tokens, "draft_tokens", torch.int32), B, int(gamma),
         _dev(cu_draft, "cu_draft", torch.int32, B + 1), V,
@@ -168,7 +160,57 @@ def spec_verify_greedy(target_logits, draft_tokens, gamma: int, out_tokens,
         _dev(out_num_accepted, "out_num_accepted", torch.int32, B),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         None if probe is None else ctypes.byref(probe), _stream(stream))
-    _check(rc, "spec_verify_greedy")
+
+
+def spec_verify_sample(target_logits, draft_logits, draft_tokens, uniforms, temperatures,
+                       gamma: int, out_tokens, out_num_accepted, workspace,
+                       cu_draft=None, probe: Optional[_Probe] = None, stream=None) -> None:
+    """Asynchronous on the current (or given) stream.  ``target_logits [R_t, V]`` and
+    ``draft_logits [R_d, V]`` share one dtype (float32 / bfloat16); ``B`` is
+    ``temperatures.numel()``; ``workspace`` is a uint8 tensor of at least
+    ``spec_verify_workspace_size`` bytes."""
+    args = _sample_args(target_logits, draft_logits, draft_tokens, uniforms, temperatures,
+                        gamma, out_tokens, out_num_accepted, workspace, cu_draft, probe, stream)
+    _check(lib().spec_verify_sample(*args), "spec_verify_sample")
+
+
+def spec_verify_greedy(target_logits, draft_tokens, gamma: int, out_tokens,
+                       out_num_accepted, workspace, cu_draft=None,
+                       probe: Optional[_Probe] = None, stream=None) -> None:
+    """Temperature-zero verification; ``B`` is ``out_num_accepted.numel()``."""
+    args = _greedy_args(target_logits, draft_tokens, gamma, out_tokens, out_num_accepted,
+                        workspace, cu_draft, probe, stream)
+    _check(lib().spec_verify_greedy(*args), "spec_verify_greedy")
+
+
+class PreparedCall:
+    """One entry-point call with its arguments checked and marshalled once.  Calling it runs
+    the entry point again on the same buffers and stream; the caller keeps the tensors (and
+    the probe) alive and refills the inputs in place between calls."""
+
+    def __init__(self, fn, args, where, keep):
+        self._fn, self._args, self._where, self._keep = fn, args, where, keep
+
+    def __call__(self) -> None:
+        _check(self._fn(*self._args), self._where)
+
+
+def prepare_sample(target_logits, draft_logits, draft_tokens, uniforms, temperatures,
+                   gamma: int, out_tokens, out_num_accepted, workspace, cu_draft=None,
+                   probe: Optional[_Probe] = None, stream=None) -> PreparedCall:
+    """``spec_verify_sample`` with the same arguments, marshalled once for repeated calls."""
+    args = _sample_args(target_logits, draft_logits, draft_tokens, uniforms, temperatures,
+                        gamma, out_tokens, out_num_accepted, workspace, cu_draft, probe, stream)
+    return PreparedCall(lib().spec_verify_sample, args, "spec_verify_sample", probe)
+
+
+def prepare_greedy(target_logits, draft_tokens, gamma: int, out_tokens, out_num_accepted,
+                   workspace, cu_draft=None, probe: Optional[_Probe] = None,
+                   stream=None) -> PreparedCall:
+    """``spec_verify_greedy`` with the same arguments, marshalled once for repeated calls."""
+    args = _greedy_args(target_logits, draft_tokens, gamma, out_tokens, out_num_accepted,
+                        workspace, cu_draft, probe, stream)
+    return PreparedCall(lib().spec_verify_greedy, args, "spec_verify_greedy", probe)
 
 
 def alloc_workspace(B: int, gamma: int, V: int, dtype: int, device="cuda"):

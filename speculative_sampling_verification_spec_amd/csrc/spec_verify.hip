@@ -5,7 +5,7 @@
 // and emit a draw from max(p_j - q_j, 0) there, or from p_gamma when nothing was rejected;
 // at temperature zero, compare each draft with the target argmax instead.
 //
-// Two or three launches on the caller's stream, none of which waits for the host:
+// Two launches on the caller's stream, neither of which waits for the host:
 //
 //  k_rowstats  The HBM-bound stream.  Every needed logit row is read exactly once, cut into
 //              16K-element tiles, one workgroup per (row slot, slice) on a 2-D grid; slots a
@@ -17,23 +17,24 @@
 //              argmax).  Output: one partial per (row, slice), and the row's logit at its
 //              draft token from the tile that holds it.
 //
-// Then a request is finished in four steps: (1) merge its row partials (one wavefront per
-// row, one lane per slice, fp64); (2) run the accept tests lane-parallel (p(x), q(x) in fp64
-// from the captured logits) and find the first rejection with ballot + find-first-set, write
-// the outputs; (3) stream the stop row(s) once more into one fp64 sum of S_t (p_k - q_k)_+
-// (or S_t p_k for the bonus) per 64-unit chunk; (4) draw: a block scan over the chunk sums
-// picks the chunk holding u * R, a wavefront scan over its 64 units picks the unit, and a walk
-// over the unit's elements gives the token.  Two ways, chosen per call by size:
-//
-//  k_finish    (many requests) one workgroup per request does steps 1-4.
-//  k_resid     (few requests with long rows) workgroups (request, 1024-unit slice of the stop
-//              row) each repeat steps 1-2 and stream their slice (step 3); then
-//  k_draw      one workgroup per request draws (step 4).
+//  k_finish    Workgroups (request, slice of the vocabulary).  Each one (1) merges its
+//              request's row partials (one wavefront per row, one lane per slice, fp64) and
+//              (2) runs the accept tests lane-parallel (p(x), q(x) in fp64 from the captured
+//              logits) with the first rejection from ballot + find-first-set; slice 0 writes
+//              the outputs.  For a sampled request every slice then (3) streams its part of the
+//              stop row(s) into one fp64 sum of S_t (p_k - q_k)_+ (or S_t p_k for the bonus) per
+//              64-unit chunk, and the last slice to finish (4) draws: a block scan over the
+//              request's chunk sums picks the chunk holding u * R, a wavefront scan over its 64
+//              units picks the unit, and a walk over the unit's elements gives the token.  The
+//              chunk sums cross workgroups as device-scope atomic stores and loads, ordered by
+//              a per-request arrival counter (which k_rowstats clears), so no cache writeback
+//              is needed inside the kernel.
 //
 // Numerics: logits convert exactly to fp32; exponent arguments carry the temperature as a
 // two-float constant, so rounding never shifts the temperature, and their shifts are kept
 // exact in fp64 when partials are combined; every sum beyond one thread's terms is fp64.
 // Merged row sums are the normaliser sum_k exp((z_k - max)/T).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -51,8 +52,10 @@ constexpr int64_t kTileElems = 16384;        // k_rowstats tile: 64 elements per
 constexpr int kMaxSlices = 64;               // finest cut of rows in small problems
 constexpr int kSmallGrid = 1024;             // below this many tiles, cut rows finer
 constexpr int64_t kMaxGridY = 65535;         // k_rowstats slots per grid row (y), z covers more
-constexpr int kFinPassUnits = 4096;         // k_finish: stop-row units per pass in flight
-constexpr int kResSliceUnits = 1024;         // k_resid: stop-row units per workgroup
+constexpr int kFinRU = 8;                    // k_finish: units per thread per row in flight
+constexpr int kFinPassUnits = kThreads * kFinRU;  // k_finish: stop-row units per pass
+constexpr int kFinGrid = 1024;               // k_finish workgroups aimed for
+constexpr int kChunkUnits = 64;              // residual sums: one per 64 units (a wavefront load)
 constexpr int64_t kMaxV = int64_t(1) << 24;
 constexpr double kLog2e = 1.4426950408889634074;
 constexpr size_t kAlign = 256;
@@ -70,8 +73,7 @@ struct alignas(16) Partial {
 
 enum : int32_t { kModeNone = 0, kModeResidual = 1, kModeBonus = 2 };
 
-// What the residual weights and the draw of a sampled request's stop row j need; on the
-// split path k_resid leaves it in the workspace for k_draw.
+// What the residual weights and the draw of a sampled request's stop row j need.
 struct alignas(16) Stop {
   int32_t mode;
   float mt, md;              // maxima of target / draft row j
@@ -92,10 +94,11 @@ struct Params {
   int32_t *out_tokens, *out_n;
   Partial *parts;
   float *gz;                // [B][spr] logit of each sampled row at its row's draft token
-  Stop *stop;               // [B] split path: stop records from k_resid for k_draw
-  int32_t nsplit_r;         // split path: k_resid workgroups per request
   double *chunk_sums;       // [B][chunk_stride] residual sums per 64-unit chunk
   int64_t chunk_stride;
+  uint32_t *done;           // [B] k_finish slices of each request finished (k_rowstats clears)
+  int32_t nslice;           // k_finish workgroups per request
+  int64_t slice_units;      // stop-row units per k_finish workgroup (a multiple of 64)
   int32_t spr;              // row slots per request: 2*gamma+1 (sample) or gamma+1 (greedy)
   int32_t nsplit;           // k_rowstats tiles (slices) per row
   int64_t split_len;        // elements per slice: one tile, or less for small problems
@@ -271,6 +274,30 @@ __device__ __forceinline__ float unit_sum(const float (&e)[W]) {
   }
 }
 
+// ------------------------------------------------------------------ data shared across workgroups
+//
+// Values one workgroup hands to another inside a kernel go through device-scope atomic stores
+// and loads, which are coherent across the XCDs' separate L2 caches without a cache writeback
+// or invalidate.  The writer waits for its stores to complete before it updates an arrival
+// counter (a device-scope atomic add); a reader loads them only after its own update of that
+// counter has returned the count that makes it the last arrival.
+__device__ __forceinline__ void share_store(double *p, double v) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long *>(p),
+                     (unsigned long long)__double_as_longlong(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double share_load(const double *p) {
+  return __longlong_as_double((long long)__hip_atomic_load(
+      reinterpret_cast<unsigned long long *>(const_cast<double *>(p)), __ATOMIC_RELAXED,
+      __HIP_MEMORY_SCOPE_AGENT));
+}
+// Block until every memory operation this thread issued has completed.
+__device__ __forceinline__ void wait_memory() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ------------------------------------------------------------------ wave / block reductions
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -431,6 +458,9 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Params P) {
     pos = i;
   }
   const int32_t tok = T > 0.f && pos < gb ? P.tokens[dbase + pos] : -1;
+  // k_finish counts its workgroups per request from zero: the first tile of the request's
+  // first target row (present in every request) clears the counter for it.
+  if (k == 0 && blockIdx.x == 0 && threadIdx.x == 0) P.done[b] = 0u;
   const int64_t lo = (int64_t)blockIdx.x * P.split_len;
   const int64_t hi = lo + P.split_len < P.V ? lo + P.split_len : P.V;
   const Store *tile = static_cast<const Store *>(row_ptr<DT>(base, row, P.V)) + lo / W;
@@ -452,7 +482,7 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Params P) {
   const float M = block_max1(tm, sh.mx);
   Partial *out = P.parts + (int64_t)slot * P.nsplit + blockIdx.x;
 
-  // The logit at the row's draft token, for k_resid's accept tests: written by the thread
+  // The logit at the row's draft token, for k_finish's accept tests: written by the thread
   // holding it, in the one tile that does.
   if (tok >= lo && tok < hi) {
     const int32_t off = (int32_t)(tok - lo);
@@ -616,7 +646,7 @@ __device__ int32_t draw_from_row(const void *tr, int64_t V, const Stop &st, doub
 
 // Merged rows of one request, in LDS.
 struct ReqLds {
-  float m[2 * SPEC_MAX_GAMMA + 1];   // row maxima: target rows 0..gb, then draft rows
+  float m[2 * SPEC_MAX_GAMMA + 1];   // row maxima by row slot: target rows 0..gamma, then drafts
   double s[2 * SPEC_MAX_GAMMA + 1];  // row sums (sampled requests)
   int32_t i[SPEC_MAX_GAMMA + 1];     // target argmax (greedy requests)
   int32_t j;                         // the stop row
@@ -626,54 +656,66 @@ struct ReqLds {
 //  1. merge the row partials (one wavefront per row, one lane per slice, fp64);
 //  2. accept tests lane-parallel on wavefront 0 (p(x), q(x) in fp64 from the logits that
 //     k_rowstats captured) and the first rejection by ballot + find-first-set.
-// With `write`, the outputs and the row probes are written.  Ends with a barrier; the stop
-// row is in L.j.  Returns the request's temperature constant.
+// Merged rows sit in L by row slot (target row r at r, draft row i at gamma + 1 + i).  With
+// `write`, the outputs and the row probes are written.  Ends with a barrier; the stop row is
+// in L.j.  Returns the request's temperature constant.
 template <int NT>
 __device__ TempConst finish_head(const Params &P, int32_t b, bool write, ReqLds &L,
                                  int64_t &dbase, int32_t &gb, bool &sampling) {
   constexpr int NW = NT / 64;
+  constexpr int G = 8;  // row slots per wavefront per round of loads
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t slot0 = (int64_t)b * P.spr;
+  const int32_t dslot = P.gamma + 1;  // slot of draft row 0
+
+  // The first round trip carries everything addressed by b alone: the request's bounds and
+  // temperature, the partials of all its row slots, and the logits captured at its draft
+  // tokens.  Only the tokens and uniforms wait for the bounds.
   float T;
   request(P, b, dbase, gb, T);
+  float zt = 0.f, zd = 0.f;
+  if (wave == 0 && lane < P.gamma && !P.greedy_all) {
+    zt = P.gz[slot0 + lane];
+    zd = P.gz[slot0 + dslot + lane];
+  }
+  Partial pv[G];
+#pragma unroll
+  for (int q = 0; q < G; ++q) {
+    const int32_t k = wave + NW * q;
+    pv[q].m = -INFINITY;
+    pv[q].idx = INT32_MAX;
+    pv[q].s = 0.0;
+    if (k < P.spr && lane < P.nsplit) pv[q] = P.parts[(slot0 + k) * P.nsplit + lane];
+  }
   sampling = T > 0.f;
   const int64_t tbase = dbase + b;
-  const int32_t ntr = gb + 1;
-  const int32_t nrows = ntr + (sampling ? gb : 0);
-  const int64_t slot0 = (int64_t)b * P.spr;
   const TempConst tc = temp_const(sampling ? T : 1.f);
-
-  // What the accept tests read besides the merged rows goes out first: lane i of wavefront 0
-  // loads draft i's token, its uniform, and the two logits at the token.
   int32_t x = -1;
-  float ux = 0.f, zt = 0.f, zd = 0.f;
+  float ux = 0.f;
   if (wave == 0 && lane < gb) {
     x = P.tokens[dbase + lane];
-    if (sampling) {
-      ux = P.uniforms[2 * (tbase + lane)];
-      zt = P.gz[slot0 + lane];
-      zd = P.gz[slot0 + P.gamma + 1 + lane];
-    }
+    if (sampling) ux = P.uniforms[2 * (tbase + lane)];
   }
 
-  // 1. Wavefront w takes rows w, w + NW, ...; lane p holds slice p.
-  for (int32_t r0 = 0; r0 < nrows; r0 += NW * 4) {
-    Partial pv[4];
+  // 1. Wavefront w takes row slots w, w + NW, ...; lane p holds slice p.
+  for (int32_t k0 = 0; k0 < P.spr; k0 += NW * G) {
+    if (k0 > 0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int32_t r = r0 + wave + NW * q;
-      pv[q].m = -INFINITY;
-      pv[q].idx = INT32_MAX;
-      pv[q].s = 0.0;
-      if (r < nrows && lane < P.nsplit) {
-        const int64_t slot = r < ntr ? slot0 + r : slot0 + P.gamma + 1 + (r - ntr);
-        pv[q] = P.parts[slot * P.nsplit + lane];
+      for (int q = 0; q < G; ++q) {
+        const int32_t k = k0 + wave + NW * q;
+        pv[q].m = -INFINITY;
+        pv[q].idx = INT32_MAX;
+        pv[q].s = 0.0;
+        if (k < P.spr && lane < P.nsplit) pv[q] = P.parts[(slot0 + k) * P.nsplit + lane];
       }
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int32_t r = r0 + wave + NW * q;
-      if (r >= nrows) break;  // uniform across the wavefront
-      const Partial *rowp = P.parts + (r < ntr ? slot0 + r : slot0 + P.gamma + 1 + (r - ntr)) * P.nsplit;
+    for (int q = 0; q < G; ++q) {
+      const int32_t k = k0 + wave + NW * q;
+      if (k >= P.spr) break;  // uniform across the wavefront
+      const bool live = k < dslot ? k <= gb : sampling && k - dslot < gb;
+      if (!live) continue;
+      const Partial *rowp = P.parts + (slot0 + k) * P.nsplit;
       if (sampling) {
         float m = pv[q].m;
         for (int32_t p = lane + 64; p < P.nsplit; p += 64) m = fmaxf(m, rowp[p].m);
@@ -687,8 +729,8 @@ __device__ TempConst finish_head(const Params &P, int32_t b, bool write, ReqLds 
         }
         const double S = wave_sum(f);
         if (lane == 0) {
-          L.m[r] = M;
-          L.s[r] = S;
+          L.m[k] = M;
+          L.s[k] = S;
         }
       } else {
         float bv = pv[q].m;
@@ -696,8 +738,8 @@ __device__ TempConst finish_head(const Params &P, int32_t b, bool write, ReqLds 
         for (int32_t p = lane + 64; p < P.nsplit; p += 64) argmax_merge(bv, bi, rowp[p].m, rowp[p].idx);
         wave_argmax(bv, bi);
         if (lane == 0) {
-          L.m[r] = bv;
-          L.i[r] = bi;
+          L.m[k] = bv;
+          L.i[k] = bi;
         }
       }
     }
@@ -714,7 +756,7 @@ __device__ TempConst finish_head(const Params &P, int32_t b, bool write, ReqLds 
       } else {
         if (x >= 0 && x < P.V) {
           p = exp2(((double)zt - (double)L.m[lane]) * tc.c) / L.s[lane];
-          q = exp2(((double)zd - (double)L.m[ntr + lane]) * tc.c) / L.s[ntr + lane];
+          q = exp2(((double)zd - (double)L.m[dslot + lane]) * tc.c) / L.s[dslot + lane];
         }
         accept = (double)ux * q < p;
       }
@@ -738,13 +780,14 @@ __device__ TempConst finish_head(const Params &P, int32_t b, bool write, ReqLds 
     }
   }
   if (write) {
-    for (int32_t r = tid; r < nrows; r += NT) {
-      if (r < ntr) {
-        if (P.row_max_t) P.row_max_t[tbase + r] = L.m[r];
-        if (sampling && P.row_sum_t) P.row_sum_t[tbase + r] = L.s[r];
-      } else {
-        if (P.row_max_d) P.row_max_d[dbase + r - ntr] = L.m[r];
-        if (P.row_sum_d) P.row_sum_d[dbase + r - ntr] = L.s[r];
+    for (int32_t r = tid; r <= gb; r += NT) {
+      if (P.row_max_t) P.row_max_t[tbase + r] = L.m[r];
+      if (sampling && P.row_sum_t) P.row_sum_t[tbase + r] = L.s[r];
+    }
+    if (sampling) {
+      for (int32_t r = tid; r < gb; r += NT) {
+        if (P.row_max_d) P.row_max_d[dbase + r] = L.m[dslot + r];
+        if (P.row_sum_d) P.row_sum_d[dbase + r] = L.s[dslot + r];
       }
     }
   }
@@ -753,9 +796,9 @@ __device__ TempConst finish_head(const Params &P, int32_t b, bool write, ReqLds 
 }
 
 // The residual weights' constants for stop row j of a sampled request.
-__device__ __forceinline__ Stop make_stop(const ReqLds &L, int32_t gb, const TempConst &tc,
-                                          int64_t trow, int64_t drow) {
-  const int32_t j = L.j, ntr = gb + 1;
+__device__ __forceinline__ Stop make_stop(const ReqLds &L, int32_t gb, int32_t dslot,
+                                          const TempConst &tc, int64_t trow, int64_t drow) {
+  const int32_t j = L.j;
   Stop st = {};
   st.mode = j < gb ? kModeResidual : kModeBonus;
   st.mt = L.m[j];
@@ -763,8 +806,8 @@ __device__ __forceinline__ Stop make_stop(const ReqLds &L, int32_t gb, const Tem
   st.c_hi = tc.c_hi;
   st.c_lo = tc.c_lo;
   if (j < gb) {
-    st.md = L.m[ntr + j];
-    const double rho = L.s[j] / L.s[ntr + j];
+    st.md = L.m[dslot + j];
+    const double rho = L.s[j] / L.s[dslot + j];
     st.rho_hi = (float)rho;
     st.rho_lo = (float)(rho - (double)st.rho_hi);
   }
@@ -774,7 +817,8 @@ __device__ __forceinline__ Stop make_stop(const ReqLds &L, int32_t gb, const Tem
 }
 
 // Step 3: units [ub, ub_end) of the stop row(s), NT * RU units per pass with all loads of a
-// pass in flight; one fp64 sum per 64-unit chunk (one wavefront-wide load) into cs.
+// pass in flight; one fp64 sum per 64-unit chunk (one wavefront-wide load) into cs.  ub is a
+// multiple of 64 units, so every chunk is summed by one wavefront.
 template <int DT, bool VEC, int NT, int RU>
 __device__ __forceinline__ void stream_chunks(const Params &P, const Stop &st, int64_t ub,
                                               int64_t ub_end, double *cs) {
@@ -803,7 +847,7 @@ __device__ __forceinline__ void stream_chunks(const Params &P, const Stop &st, i
       resid_weights<W>(zt, zd, st, r);
       const float us = unit_sum<W>(r);
       const double sum = wave_sum(c0 + lane < ub_end ? (double)us : 0.0);
-      if (lane == 0) cs[c0 / 64] = sum;
+      if (lane == 0) share_store(&cs[c0 / kChunkUnits], sum);
     }
   }
 }
@@ -817,7 +861,8 @@ struct DrawLds {
   double local;
 };
 
-// Step 4, the draw, by a workgroup of NT threads once every chunk sum of request b is in cs:
+// Step 4, the draw, by a workgroup of NT threads once every chunk sum of request b is in cs
+// (written by other workgroups, so read with device-scope loads):
 // a block scan over the chunk sums picks the chunk holding u * R, a wavefront scan over its
 // 64 units picks the unit, and a walk over the unit's elements gives the token.
 template <int DT, bool VEC, int NT>
@@ -840,7 +885,7 @@ __device__ void draw_token(const Params &P, int32_t b, const Stop &st, const dou
   const int64_t a = tid * per;
   const int64_t e_ = a + per < nchunks ? a + per : nchunks;
   double mine = 0.0;
-  for (int64_t c = a; c < e_; ++c) mine += cs[c];
+  for (int64_t c = a; c < e_; ++c) mine += share_load(&cs[c]);
   double R;
   const double before = block_excl_scan<NW>(mine, D.shd, R);
   const double target = u * R;
@@ -856,7 +901,7 @@ __device__ void draw_token(const Params &P, int32_t b, const Stop &st, const dou
     double run = before;
     int64_t lastpos = -1;
     for (int64_t c = a; c < e_; ++c) {
-      const double v = cs[c];
+      const double v = share_load(&cs[c]);
       if (v > 0.0) {
         lastpos = c;
         if (first != INT32_MAX && run + v > target) {
@@ -921,68 +966,43 @@ __device__ void draw_token(const Params &P, int32_t b, const Stop &st, const dou
   }
 }
 
-// ------------------------------------------------------------------ k_finish (fused path)
+// ------------------------------------------------------------------ k_finish
 
-// One workgroup of NT threads per request does all of steps 1-4; the chunk sums it writes are
-// read back by the same workgroup after a barrier.  Used when one workgroup can stream a stop
-// row pair about as fast as the whole GPU could share it out, counting the two launches the
-// split path adds.
-template <int DT, bool VEC, int NT>
-__global__ __launch_bounds__(NT) void k_finish(Params P) {
-  constexpr int W = Unit<DT, VEC>::W;
-  __shared__ ReqLds L;
-  __shared__ DrawLds<NT / 64> D;
-  const int32_t b = (int32_t)blockIdx.x;
-  int64_t dbase;
-  int32_t gb;
-  bool sampling;
-  const TempConst tc = finish_head<NT>(P, b, true, L, dbase, gb, sampling);
-  if (!sampling) return;
-  const Stop st = make_stop(L, gb, tc, dbase + b + L.j, dbase + L.j);
-  double *cs = P.chunk_sums + (int64_t)b * P.chunk_stride;
-  stream_chunks<DT, VEC, NT, kFinPassUnits / NT>(P, st, 0, (P.V + W - 1) / W, cs);
-  __syncthreads();  // the chunk sums are read below by other wavefronts of this workgroup
-  draw_token<DT, VEC, NT>(P, b, st, cs, D);
-}
-
-// ------------------------------------------------------------------ split path
-
-// k_resid: workgroups (request, slice of kResSliceUnits units of the stop row).  Every
-// workgroup of a request repeats steps 1-2 (cheap next to the stream, and it saves a launch);
-// slice 0 writes the outputs and the stop record for k_draw.  Sampled requests then stream
-// their slice (step 3).
+// Workgroups (slice, request): blockIdx.x is the slice of the vocabulary, blockIdx.y +
+// blockIdx.z * gridDim.y the request.  Every workgroup of a sampled request repeats steps 1-2
+// (a few KB of partials, cheaper than another launch); slice 0 writes the outputs.  Then each
+// streams its slice of the stop row(s) (step 3), publishes its chunk sums and counts itself
+// in; the last one draws (step 4).  Greedy requests finish in slice 0 after step 2.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_resid(Params P) {
+__global__ __launch_bounds__(kThreads) void k_finish(Params P) {
   constexpr int W = Unit<DT, VEC>::W;
   __shared__ ReqLds L;
-  const int32_t b = (int32_t)(blockIdx.x / P.nsplit_r);
-  const int32_t split = (int32_t)(blockIdx.x % P.nsplit_r);
+  __shared__ DrawLds<kWaves> D;
+  __shared__ int32_t s_last;
+  const uint32_t b32 = blockIdx.y + blockIdx.z * gridDim.y;
+  if (b32 >= (uint32_t)P.B) return;
+  const int32_t b = (int32_t)b32;
+  const int32_t split = (int32_t)blockIdx.x;
+  if (split != 0 && (P.greedy_all || !(P.temps[b] > 0.f))) return;
   int64_t dbase;
   int32_t gb;
   bool sampling;
   const TempConst tc = finish_head<kThreads>(P, b, split == 0, L, dbase, gb, sampling);
   if (!sampling) return;
-  const Stop st = make_stop(L, gb, tc, dbase + b + L.j, dbase + L.j);
-  if (split == 0 && threadIdx.x == 0) P.stop[b] = st;
+  const Stop st = make_stop(L, gb, P.gamma + 1, tc, dbase + b + L.j, dbase + L.j);
   const int64_t nunits = (P.V + W - 1) / W;
-  const int64_t ub = (int64_t)split * kResSliceUnits;
-  const int64_t ue = ub + kResSliceUnits < nunits ? ub + kResSliceUnits : nunits;
-  stream_chunks<DT, VEC, kThreads, kResSliceUnits / kThreads>(P, st, ub, ue,
-                                                              P.chunk_sums + (int64_t)b * P.chunk_stride);
-}
-
-// k_draw: one workgroup per request, step 4 from k_resid's stop record and chunk sums.
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_draw(Params P) {
-  __shared__ DrawLds<kWaves> D;
-  const int32_t b = (int32_t)blockIdx.x;
-  int64_t dbase;
-  int32_t gb;
-  float T;
-  request(P, b, dbase, gb, T);
-  if (!(T > 0.f)) return;
-  const Stop st = P.stop[b];
-  draw_token<DT, VEC, kThreads>(P, b, st, P.chunk_sums + (int64_t)b * P.chunk_stride, D);
+  const int64_t ub = (int64_t)split * P.slice_units;
+  const int64_t ue = ub + P.slice_units < nunits ? ub + P.slice_units : nunits;
+  double *cs = P.chunk_sums + (int64_t)b * P.chunk_stride;
+  stream_chunks<DT, VEC, kThreads, kFinRU>(P, st, ub, ue, cs);
+  wait_memory();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(&P.done[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (uint32_t)P.nslice - 1u;
+  __syncthreads();
+  if (!s_last) return;
+  draw_token<DT, VEC, kThreads>(P, b, st, cs, D);
 }
 
 // ------------------------------------------------------------------ host side
@@ -990,9 +1010,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(Params P) {
 struct Plan {
   int32_t spr, nsplit;
   int64_t split_len, chunk_stride;
-  bool fused;               // finishing path: k_finish, or k_resid + k_draw
-  int32_t fin_threads;      // k_finish workgroup size
-  size_t off_parts, off_gz, off_stop, off_chunks, total;
+  size_t off_parts, off_gz, off_chunks, off_done, total;
 };
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -1017,26 +1035,15 @@ bool make_plan(int32_t B, int32_t gamma, int64_t V, int dtype, bool greedy, Plan
   }
   pl.nsplit = (int32_t)ceil_div(V, len);  // no empty slice
   pl.split_len = len;
-  // Finishing path.  One workgroup streams a request's stop row pair at about what one CU
-  // draws (~25 GB/s on MI355X); the split path shares all stop rows out over the GPU
-  // (~6 TB/s) but adds two launches (~8 us).  Greedy requests stream nothing.
-  const double pair = 2.0 * (double)V * (dtype == SPEC_F32 ? 4 : 2);
-  pl.fused = greedy || pair / 25e9 <= (double)bb * pair / 6e12 + 8e-6;
-  pl.fin_threads = bb > 256 ? 512 : 1024;
   // Chunk sums of the stop rows; the element path (one element per unit) has the most chunks.
-  pl.chunk_stride = ceil_div(V, 64);
+  pl.chunk_stride = ceil_div(V, kChunkUnits);
   pl.off_parts = 0;
   pl.off_gz = align_up((size_t)bb * pl.spr * pl.nsplit * sizeof(Partial));
-  pl.off_stop = pl.off_gz + (greedy ? 0 : align_up((size_t)bb * pl.spr * sizeof(float)));
-  pl.off_chunks = pl.off_stop + (pl.fused ? 0 : align_up((size_t)bb * sizeof(Stop)));
-  pl.total = pl.off_chunks + (greedy ? 0 : align_up((size_t)bb * pl.chunk_stride * sizeof(double)));
+  pl.off_chunks = pl.off_gz + (greedy ? 0 : align_up((size_t)bb * pl.spr * sizeof(float)));
+  pl.off_done = pl.off_chunks +
+                (greedy ? 0 : align_up((size_t)bb * pl.chunk_stride * sizeof(double)));
+  pl.total = pl.off_done + align_up((size_t)bb * sizeof(uint32_t));
   return true;
-}
-
-int record(const spec_probe *probe, int k, hipStream_t s) {
-  if (!probe || !probe->events[k]) return SPEC_OK;
-  return hipEventRecord((hipEvent_t)probe->events[k], s) == hipSuccess ? SPEC_OK
-                                                                       : SPEC_ERR_HIP;
 }
 
 #define SPEC_TRY(expr)              \
@@ -1045,34 +1052,40 @@ int record(const spec_probe *probe, int k, hipStream_t s) {
     if (rc_ != SPEC_OK) return rc_; \
   } while (0)
 
-int launched() { return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP; }
+// Launch kernel k of the call.  With probe events for it, the dispatch itself records them
+// (hipExtLaunchKernel), so timing adds no marker packets, and no idle time, to the stream.
+template <typename K>
+int launch(K kernel, dim3 grid, const spec_probe *probe, int k, hipStream_t s, Params &P) {
+  hipEvent_t e0 = probe ? static_cast<hipEvent_t>(probe->events[2 * k]) : nullptr;
+  hipEvent_t e1 = probe ? static_cast<hipEvent_t>(probe->events[2 * k + 1]) : nullptr;
+  if (!e0 && !e1) {
+    kernel<<<grid, dim3(kThreads), 0, s>>>(P);
+    return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+  }
+  void *args[] = {&P};
+  return hipExtLaunchKernel(reinterpret_cast<const void *>(kernel), grid, dim3(kThreads), args, 0,
+                            s, e0, e1, 0) == hipSuccess
+             ? SPEC_OK
+             : SPEC_ERR_HIP;
+}
 
 template <int DT, bool VEC>
 int run(Params P, const Plan &pl, const spec_probe *probe, hipStream_t s) {
   const int64_t slots = (int64_t)P.B * pl.spr;
   const uint32_t gy = (uint32_t)(slots < kMaxGridY ? slots : kMaxGridY);
   const uint32_t gz = (uint32_t)ceil_div(slots, gy);
-  const dim3 grid_b((uint32_t)P.B);
-  SPEC_TRY(record(probe, 0, s));
-  k_rowstats<DT, VEC><<<dim3((uint32_t)pl.nsplit, gy, gz), dim3(kThreads), 0, s>>>(P);
-  SPEC_TRY(launched());
-  SPEC_TRY(record(probe, 1, s));
-  SPEC_TRY(record(probe, 2, s));
-  if (pl.fused) {
-    if (pl.fin_threads == 512) k_finish<DT, VEC, 512><<<grid_b, dim3(512), 0, s>>>(P);
-    else k_finish<DT, VEC, 1024><<<grid_b, dim3(1024), 0, s>>>(P);
-    SPEC_TRY(launched());
-    SPEC_TRY(record(probe, 3, s));
-  } else {
-    P.nsplit_r = (int32_t)ceil_div(ceil_div(P.V, Unit<DT, VEC>::W), kResSliceUnits);
-    k_resid<DT, VEC><<<dim3((uint32_t)((int64_t)P.B * P.nsplit_r)), dim3(kThreads), 0, s>>>(P);
-    SPEC_TRY(launched());
-    SPEC_TRY(record(probe, 3, s));
-    SPEC_TRY(record(probe, 4, s));
-    k_draw<DT, VEC><<<grid_b, dim3(kThreads), 0, s>>>(P);
-    SPEC_TRY(launched());
-    SPEC_TRY(record(probe, 5, s));
-  }
+  // k_finish: enough slices of the stop rows per request for about kFinGrid workgroups, each
+  // at least one pass and a whole number of 64-unit chunks.  Greedy calls need slice 0 only.
+  const int64_t nunits = ceil_div(P.V, Unit<DT, VEC>::W);
+  int64_t want = P.greedy_all ? 1 : ceil_div(kFinGrid, P.B);
+  const int64_t most = ceil_div(nunits, kFinPassUnits);
+  if (want > most) want = most;
+  P.slice_units = ceil_div(ceil_div(nunits, want), kChunkUnits) * kChunkUnits;
+  P.nslice = (int32_t)ceil_div(nunits, P.slice_units);
+  const uint32_t fy = (uint32_t)(P.B < kMaxGridY ? P.B : kMaxGridY);
+  const uint32_t fz = (uint32_t)ceil_div(P.B, fy);
+  SPEC_TRY(launch(k_rowstats<DT, VEC>, dim3((uint32_t)pl.nsplit, gy, gz), probe, 0, s, P));
+  SPEC_TRY(launch(k_finish<DT, VEC>, dim3((uint32_t)P.nslice, fy, fz), probe, 1, s, P));
   return SPEC_OK;
 }
 
@@ -1092,10 +1105,7 @@ int setup(Params &P, const Plan &pl, void *workspace, size_t workspace_bytes) {
   char *ws = static_cast<char *>(workspace);
   P.parts = reinterpret_cast<Partial *>(ws + pl.off_parts);
   P.gz = reinterpret_cast<float *>(ws + pl.off_gz);
-  P.stop = reinterpret_cast<Stop *>(ws + pl.off_stop);
-  // the split path's grid, for the widest case (one element per unit)
-  if (!pl.fused && (int64_t)P.B * ceil_div(P.V, kResSliceUnits) > (int64_t)UINT32_MAX)
-    return SPEC_ERR_SHAPE;
+  P.done = reinterpret_cast<uint32_t *>(ws + pl.off_done);
   P.chunk_sums = reinterpret_cast<double *>(ws + pl.off_chunks);
   P.chunk_stride = pl.chunk_stride;
   P.spr = pl.spr;
@@ -1128,7 +1138,7 @@ const char *spec_verify_strerror(int code) {
       return "invalid sizes (B < 0, gamma outside [0, 64], V outside [1, 2^24], or grid too large)";
     case SPEC_ERR_DTYPE: return "dtype is neither SPEC_F32 nor SPEC_BF16";
     case SPEC_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
-    case SPEC_ERR_HIP: return "HIP kernel launch or event record failed";
+    case SPEC_ERR_HIP: return "HIP kernel launch failed";
     default: return "unknown spec_verify error code";
   }
 }

@@ -76,19 +76,20 @@ def test_long_rows_with_multi_tile_slices():
     _both(w)
 
 
-@pytest.mark.parametrize("B,gamma,V,dtype,launch_count", [
-    (300, 2, 4096, "bf16", 2),      # many requests, short rows: one workgroup per request
-    (5, 3, 16, "f32", 2),
-    (2, 3, 300_000, "bf16", 3),     # few requests, long rows: stop rows shared out
-    (3, 2, 250_001, "f32", 3),      # ... on the element path
+@pytest.mark.parametrize("B,gamma,V,dtype", [
+    (300, 2, 4096, "bf16"),      # many requests, short rows: one slice per request
+    (5, 3, 16, "f32"),           # a single chunk
+    (2, 3, 300_000, "bf16"),     # few requests, long rows: many slices per request
+    (3, 2, 250_001, "f32"),      # ... on the element path
+    (1, 1, 65_536, "f32"),       # one request: its slices alone make the grid
 ])
-def test_both_finishing_paths(B, gamma, V, dtype, launch_count):
-    # the library finishes requests either in one launch per request (k_finish) or in two
-    # (k_resid over slices of the stop rows, then k_draw); both must match the oracle
+def test_sliced_finish(B, gamma, V, dtype):
+    # every call is two launches: row statistics, then k_finish over (slice, request), whose
+    # last slice per request draws; the number of slices follows B and V
     temps = np.where(np.arange(B) % 4 == 1, 0.0, np.linspace(0.4, 1.4, B))
     w = workloads.small(B=B, gamma=gamma, V=V, dtype=dtype, seed=B * 7 + V, ragged=True,
                         temperatures=temps, draft_sigma=0.9)
-    assert launches(w) == launch_count
+    assert launches(w) == 2
     _both(w)
     assert launches(w, greedy=True) == 2
     _both(w, greedy=True)
@@ -254,6 +255,54 @@ def test_repeated_calls_are_bit_identical():
     b = run(w, dev=d)
     for k in a:
         np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_one_workspace_across_shapes_needs_no_clearing():
+    # the workspace holds the per-request arrival counters of k_finish; it is filled with
+    # 0xff once and then reused by calls of different sizes, which must still match the oracle
+    import torch
+    import speculative_sampling_verification_spec_amd as sv
+    shapes = [(40, 5, 30000, "bf16"), (3, 8, 70001, "f32"), (64, 2, 4096, "bf16"),
+              (40, 5, 30000, "bf16")]
+    need = max(sv.spec_verify_workspace_size(B, g, V, sv.SPEC_BF16 if dt == "bf16" else sv.SPEC_F32)
+               for B, g, V, dt in shapes)
+    ws = torch.full((need,), 0xff, dtype=torch.uint8, device="cuda")
+    for i, (B, gamma, V, dtype) in enumerate(shapes):
+        temps = np.where(np.arange(B) % 5 == 2, 0.0, np.linspace(0.5, 1.3, B))
+        w = workloads.small(B=B, gamma=gamma, V=V, dtype=dtype, seed=300 + i, ragged=True,
+                            temperatures=temps, draft_sigma=1.0)
+        print(f"[gpu] shared workspace call {i}: B={B} gamma={gamma} V={V} {dtype}", flush=True)
+        g = run(w, workspace=ws)
+        parity.compare(w, g, oracle.verify(w))
+
+
+def test_prepared_call_repeats_the_entry_point():
+    # a call marshalled once and run twice gives what the plain call gives
+    import torch
+    import speculative_sampling_verification_spec_amd as sv
+    w = workloads.small(B=20, gamma=4, V=9000, dtype="bf16", seed=88, ragged=True,
+                        temperatures=np.linspace(0.0, 1.1, 20))
+    d = to_device(w)
+    ref = run(w, dev=d, probe=False)
+    ws = sv.alloc_workspace(w.B, w.gamma, w.V, sv.SPEC_BF16)
+    out = torch.full((w.R_t,), -7, dtype=torch.int32, device="cuda")
+    nacc = torch.full((w.B,), -7, dtype=torch.int32, device="cuda")
+    call = sv.prepare_sample(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temps"],
+                             w.gamma, out, nacc, ws, cu_draft=d["cu"])
+    for _ in range(2):
+        out.fill_(-7)
+        call()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(out.cpu().numpy(), ref["out_tokens"])
+        np.testing.assert_array_equal(nacc.cpu().numpy(), ref["num_accepted"])
+    g = w.as_greedy()
+    dg = to_device(g)
+    refg = run(g, greedy=True, dev=dg, probe=False)
+    callg = sv.prepare_greedy(dg["target"], dg["tokens"], g.gamma, out, nacc, ws, cu_draft=dg["cu"])
+    callg()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), refg["out_tokens"])
+    np.testing.assert_array_equal(nacc.cpu().numpy(), refg["num_accepted"])
 
 
 # ----------------------------------------------------------------------- distribution
