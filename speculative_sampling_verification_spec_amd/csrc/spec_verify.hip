@@ -48,11 +48,13 @@ namespace {
 
 constexpr int kThreads = 256;                // 4 wavefronts of 64
 constexpr int kWaves = kThreads / 64;
-constexpr int64_t kTileElems = 16384;        // k_rowstats tile: 64 elements per thread
+constexpr int64_t kTileElems = 16384;        // k_rowstats tile
+constexpr int kRsThreads = 256;              // k_rowstats workgroup: 64 elements per thread
+constexpr int kRsWaves = kRsThreads / 64;
 constexpr int kMaxSlices = 64;               // finest cut of rows in small problems
 constexpr int kSmallGrid = 1024;             // below this many tiles, cut rows finer
 constexpr int64_t kMaxGridY = 65535;         // k_rowstats slots per grid row (y), z covers more
-constexpr int kFinRU = 8;                    // k_finish: units per thread per row in flight
+constexpr int kFinRU = 4;                    // k_finish: units per thread per row in flight
 constexpr int kFinPassUnits = kThreads * kFinRU;  // k_finish: stop-row units per pass
 constexpr int kFinGrid = 1024;               // k_finish workgroups aimed for
 constexpr int kChunkUnits = 64;              // residual sums: one per 64 units (a wavefront load)
@@ -72,6 +74,16 @@ struct alignas(16) Partial {
 };
 
 enum : int32_t { kModeNone = 0, kModeResidual = 1, kModeBonus = 2 };
+
+// Per row slot, from k_rowstats for k_finish's accept tests: the row's logit at its draft
+// token (sampled rows), and for target rows 0..gamma_b-1 the draft token and its accept
+// uniform, so k_finish reads all of them in its first round trip.
+struct alignas(16) SlotRec {
+  float z;
+  int32_t tok;
+  float u;
+  int32_t pad;
+};
 
 // What the residual weights and the draw of a sampled request's stop row j need.
 struct alignas(16) Stop {
@@ -93,7 +105,7 @@ struct Params {
   int64_t V;
   int32_t *out_tokens, *out_n;
   Partial *parts;
-  float *gz;                // [B][spr] logit of each sampled row at its row's draft token
+  SlotRec *rec;             // [B][spr] per row slot: logit at the draft token, token, uniform
   double *chunk_sums;       // [B][chunk_stride] residual sums per 64-unit chunk
   int64_t chunk_stride;
   uint32_t *done;           // [B] k_finish slices of each request finished (k_rowstats clears)
@@ -321,14 +333,6 @@ __device__ __forceinline__ void argmax_merge(float &bv, int32_t &bi, float ov, i
     bi = oi;
   }
 }
-__device__ __forceinline__ void wave_argmax(float &bv, int32_t &bi) {
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(bv, o);
-    const int32_t oi = __shfl_xor(bi, o);
-    argmax_merge(bv, bi, ov, oi);
-  }
-}
-
 // Inclusive scan over a wavefront (fp64, lane order).
 __device__ __forceinline__ double wave_incl_scan(double v) {
   const int lane = threadIdx.x & 63;
@@ -341,31 +345,34 @@ __device__ __forceinline__ double wave_incl_scan(double v) {
 
 // Block reductions with one barrier each.  Every call site owns its LDS array, and the next
 // write to that array is separated from these reads by another reduction's barrier.
+template <int NW>
 __device__ __forceinline__ float block_max1(float v, float *sh) {
   v = wave_max(v);
   if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
   __syncthreads();
   float r = sh[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) r = fmaxf(r, sh[i]);
+  for (int i = 1; i < NW; ++i) r = fmaxf(r, sh[i]);
   return r;
 }
+template <int NW>
 __device__ __forceinline__ double block_sum1(double v, double *sh) {
   v = wave_sum(v);
   if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
   __syncthreads();
   double r = sh[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) r += sh[i];
+  for (int i = 1; i < NW; ++i) r += sh[i];
   return r;
 }
+template <int NW>
 __device__ __forceinline__ int32_t block_min1(int32_t v, int32_t *sh) {
   v = wave_min_i(v);
   if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
   __syncthreads();
   int32_t r = sh[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) r = sh[i] < r ? sh[i] : r;
+  for (int i = 1; i < NW; ++i) r = sh[i] < r ? sh[i] : r;
   return r;
 }
 
@@ -417,20 +424,22 @@ __device__ int32_t block_last(bool pred, int32_t *sh) {
 // ------------------------------------------------------------------ k_rowstats
 
 struct StatsLds {
-  float mx[kWaves];
-  double sum[kWaves];
-  int32_t idx[kWaves];
+  float mx[kRsWaves];
+  double sum[kRsWaves];
+  int32_t idx[kRsWaves];
 };
 
 // One workgroup per (row slot, tile): blockIdx.x is the tile of the row, blockIdx.y +
 // blockIdx.z * gridDim.y the row slot (request * spr + slot).  Slots beyond a request's rows
 // (gamma_b < gamma, or draft rows of a greedy request) exit at once.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_rowstats(Params P) {
+__global__ __launch_bounds__(kRsThreads) void k_rowstats(Params P) {
   using U = Unit<DT, VEC>;
   using Store = typename U::Store;
   constexpr int W = U::W;
-  constexpr int NV = int(kTileElems / kThreads) / W;  // units per thread
+  constexpr int NT = kRsThreads;
+  constexpr int NW = kRsWaves;
+  constexpr int NV = int(kTileElems / NT) / W;  // units per thread
   __shared__ StatsLds sh;
   const int tid = threadIdx.x;
   const uint32_t slot = blockIdx.y + blockIdx.z * gridDim.y;
@@ -457,7 +466,12 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Params P) {
     row = dbase + i;
     pos = i;
   }
-  const int32_t tok = T > 0.f && pos < gb ? P.tokens[dbase + pos] : -1;
+  const int32_t xtok = pos < gb ? P.tokens[dbase + pos] : -1;
+  const int32_t tok = T > 0.f ? xtok : -1;
+  if (k <= P.gamma && pos < gb && blockIdx.x == 0 && tid == 0) {
+    P.rec[slot].tok = xtok;
+    P.rec[slot].u = T > 0.f ? P.uniforms[2 * (dbase + b + pos)] : 0.f;
+  }
   // k_finish counts its workgroups per request from zero: the first tile of the request's
   // first target row (present in every request) clears the counter for it.
   if (k == 0 && blockIdx.x == 0 && threadIdx.x == 0) P.done[b] = 0u;
@@ -468,18 +482,18 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Params P) {
 
   // The tile's loads go out before anything else; units past the row end hold the filler.
   typename U::Raw raw[NV];
-  if (nu == kThreads * NV) {
+  if (nu == NT * NV) {
 #pragma unroll
-    for (int j = 0; j < NV; ++j) raw[j] = U::template load<true>(tile, j * kThreads + tid);
+    for (int j = 0; j < NV; ++j) raw[j] = U::template load<true>(tile, j * NT + tid);
   } else {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const int32_t u = j * kThreads + tid;
+      const int32_t u = j * NT + tid;
       raw[j] = u < nu ? U::template load<true>(tile, u) : U::filler();
     }
   }
   const float tm = U::thread_max(raw);
-  const float M = block_max1(tm, sh.mx);
+  const float M = block_max1<NW>(tm, sh.mx);
   Partial *out = P.parts + (int64_t)slot * P.nsplit + blockIdx.x;
 
   // The logit at the row's draft token, for k_finish's accept tests: written by the thread
@@ -487,11 +501,11 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Params P) {
   if (tok >= lo && tok < hi) {
     const int32_t off = (int32_t)(tok - lo);
     const int32_t uo = off / W;
-    if (uo % kThreads == tid) {
+    if (uo % NT == tid) {
       float z = 0.f;
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
-        if (j == uo / kThreads) {
+        if (j == uo / NT) {
           float xv[W];
           U::cvt(raw[j], xv);
 #pragma unroll
@@ -499,7 +513,7 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Params P) {
             if (q == off % W) z = xv[q];
         }
       }
-      P.gz[slot] = z;
+      P.rec[slot].z = z;
     }
   }
 
@@ -526,7 +540,7 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Params P) {
 #pragma unroll
         for (int j = 0; j + st < NV; j += 2 * st) us[j] += us[j + st];
       }
-      const double S = block_sum1((double)us[0], sh.sum);
+      const double S = block_sum1<NW>((double)us[0], sh.sum);
       // to the shifted form, sum 2^((z - M) c): factor 2^(K - M c), one rounding
       if (tid == 0) *out = Partial{M, 0, S * exp2(fma(-(double)M, tc.c, (double)K))};
     } else {
@@ -535,7 +549,7 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Params P) {
       double acc = 0.0;
 #pragma unroll 1
       for (int j = 0; j < NV; ++j) {
-        const int32_t u = j * kThreads + tid;
+        const int32_t u = j * NT + tid;
         if (u < nu) {
           float x[W], e[W];
           U::cvt(U::template load<false>(tile, u), x);
@@ -544,7 +558,7 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Params P) {
           acc += (double)unit_sum<W>(e);
         }
       }
-      const double S = block_sum1(acc, sh.sum);
+      const double S = block_sum1<NW>(acc, sh.sum);
       if (tid == 0) *out = Partial{M, 0, S};
     }
   } else {
@@ -556,13 +570,13 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Params P) {
       for (int j = 0; j < NV; ++j) {
         float x[W];
         U::cvt(raw[j], x);
-        const int32_t u = j * kThreads + tid;
+        const int32_t u = j * NT + tid;
 #pragma unroll
         for (int q = 0; q < W; ++q)
           if (ti == INT32_MAX && u < nu && x[q] == M) ti = (int32_t)((lo / W + u) * W + q);
       }
     }
-    const int32_t bi = block_min1(ti, sh.idx);
+    const int32_t bi = block_min1<NW>(ti, sh.idx);
     if (tid == 0) *out = Partial{M, bi, 0.0};
   }
 }
@@ -653,7 +667,7 @@ struct ReqLds {
 };
 
 // Steps 1 and 2 of finishing request b, for a workgroup of NT threads:
-//  1. merge the row partials (one wavefront per row, one lane per slice, fp64);
+//  1. merge the row partials (a group of lanes per row slot, one lane per tile, fp64);
 //  2. accept tests lane-parallel on wavefront 0 (p(x), q(x) in fp64 from the logits that
 //     k_rowstats captured) and the first rejection by ballot + find-first-set.
 // Merged rows sit in L by row slot (target row r at r, draft row i at gamma + 1 + i).  With
@@ -663,81 +677,95 @@ template <int NT>
 __device__ TempConst finish_head(const Params &P, int32_t b, bool write, ReqLds &L,
                                  int64_t &dbase, int32_t &gb, bool &sampling) {
   constexpr int NW = NT / 64;
-  constexpr int G = 8;  // row slots per wavefront per round of loads
+  constexpr int G = 4;  // rounds of row slots whose partials are loaded at once
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t slot0 = (int64_t)b * P.spr;
   const int32_t dslot = P.gamma + 1;  // slot of draft row 0
 
-  // The first round trip carries everything addressed by b alone: the request's bounds and
-  // temperature, the partials of all its row slots, and the logits captured at its draft
-  // tokens.  Only the tokens and uniforms wait for the bounds.
+  // Row slots are merged in lane groups: LP lanes per slot (the smallest power of two >= the
+  // tiles per row, at most 64), R = 64 / LP slots per wavefront at a time; lane l of a group
+  // holds tiles l, l + LP, ... of its slot.
+  int32_t lp = 1;
+  while (lp < P.nsplit && lp < 64) lp <<= 1;
+  const int32_t R = 64 / lp;
+  const int32_t grp = lane / lp, sl = lane - grp * lp;
+  const int32_t per_round = NW * R;  // slots merged per round by the workgroup
+
+  // One round trip carries everything: the request's bounds and temperature, the partials
+  // of its row slots (up to G rounds), and the slot records (logits at the draft tokens, the
+  // tokens, their uniforms) that k_rowstats left.
   float T;
   request(P, b, dbase, gb, T);
-  float zt = 0.f, zd = 0.f;
-  if (wave == 0 && lane < P.gamma && !P.greedy_all) {
-    zt = P.gz[slot0 + lane];
-    zd = P.gz[slot0 + dslot + lane];
+  SlotRec rt = {};
+  float zd = 0.f;
+  if (wave == 0 && lane < P.gamma) {
+    rt = P.rec[slot0 + lane];
+    if (!P.greedy_all) zd = P.rec[slot0 + dslot + lane].z;
   }
   Partial pv[G];
 #pragma unroll
   for (int q = 0; q < G; ++q) {
-    const int32_t k = wave + NW * q;
+    const int32_t k = q * per_round + wave * R + grp;
     pv[q].m = -INFINITY;
     pv[q].idx = INT32_MAX;
     pv[q].s = 0.0;
-    if (k < P.spr && lane < P.nsplit) pv[q] = P.parts[(slot0 + k) * P.nsplit + lane];
+    if (k < P.spr && sl < P.nsplit) pv[q] = P.parts[(slot0 + k) * P.nsplit + sl];
   }
   sampling = T > 0.f;
   const int64_t tbase = dbase + b;
   const TempConst tc = temp_const(sampling ? T : 1.f);
-  int32_t x = -1;
-  float ux = 0.f;
-  if (wave == 0 && lane < gb) {
-    x = P.tokens[dbase + lane];
-    if (sampling) ux = P.uniforms[2 * (tbase + lane)];
-  }
+  const int32_t x = lane < gb ? rt.tok : -1;
+  const float ux = rt.u, zt = rt.z;
 
-  // 1. Wavefront w takes row slots w, w + NW, ...; lane p holds slice p.
-  for (int32_t k0 = 0; k0 < P.spr; k0 += NW * G) {
-    if (k0 > 0) {
+  // 1. Merge: maximum, then the sum with each tile's shift taken out in fp64 (sampled), or
+  // the lowest-index argmax (greedy), reduced over the lane group.
+  for (int32_t r0 = 0; r0 < P.spr; r0 += G * per_round) {
+    if (r0 > 0) {
 #pragma unroll
       for (int q = 0; q < G; ++q) {
-        const int32_t k = k0 + wave + NW * q;
+        const int32_t k = r0 + q * per_round + wave * R + grp;
         pv[q].m = -INFINITY;
         pv[q].idx = INT32_MAX;
         pv[q].s = 0.0;
-        if (k < P.spr && lane < P.nsplit) pv[q] = P.parts[(slot0 + k) * P.nsplit + lane];
+        if (k < P.spr && sl < P.nsplit) pv[q] = P.parts[(slot0 + k) * P.nsplit + sl];
       }
     }
 #pragma unroll
     for (int q = 0; q < G; ++q) {
-      const int32_t k = k0 + wave + NW * q;
-      if (k >= P.spr) break;  // uniform across the wavefront
-      const bool live = k < dslot ? k <= gb : sampling && k - dslot < gb;
-      if (!live) continue;
-      const Partial *rowp = P.parts + (slot0 + k) * P.nsplit;
+      if (r0 + q * per_round >= P.spr) break;  // uniform across the workgroup
+      const int32_t k = r0 + q * per_round + wave * R + grp;
+      const bool live = k < P.spr && (k < dslot ? k <= gb : sampling && k - dslot < gb);
+      const Partial *rowp = P.parts + (slot0 + (k < P.spr ? k : 0)) * P.nsplit;
       if (sampling) {
-        float m = pv[q].m;
-        for (int32_t p = lane + 64; p < P.nsplit; p += 64) m = fmaxf(m, rowp[p].m);
-        const float M = wave_max(m);
-        double f = pv[q].m != -INFINITY
-                       ? pv[q].s * exp2(((double)pv[q].m - (double)M) * tc.c)
-                       : 0.0;
-        for (int32_t p = lane + 64; p < P.nsplit; p += 64) {
-          const Partial o = rowp[p];
-          if (o.m != -INFINITY) f += o.s * exp2(((double)o.m - (double)M) * tc.c);
+        float m = live ? pv[q].m : -INFINITY;
+        if (live)
+          for (int32_t p = sl + lp; p < P.nsplit; p += lp) m = fmaxf(m, rowp[p].m);
+        for (int o = lp >> 1; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+        const float M = m;
+        double f = 0.0;
+        if (live) {
+          if (pv[q].m != -INFINITY) f = pv[q].s * exp2(((double)pv[q].m - (double)M) * tc.c);
+          for (int32_t p = sl + lp; p < P.nsplit; p += lp) {
+            const Partial o = rowp[p];
+            if (o.m != -INFINITY) f += o.s * exp2(((double)o.m - (double)M) * tc.c);
+          }
         }
-        const double S = wave_sum(f);
-        if (lane == 0) {
+        for (int o = lp >> 1; o > 0; o >>= 1) f += __shfl_xor(f, o);
+        if (live && sl == 0) {
           L.m[k] = M;
-          L.s[k] = S;
+          L.s[k] = f;
         }
       } else {
-        float bv = pv[q].m;
-        int32_t bi = pv[q].idx;
-        for (int32_t p = lane + 64; p < P.nsplit; p += 64) argmax_merge(bv, bi, rowp[p].m, rowp[p].idx);
-        wave_argmax(bv, bi);
-        if (lane == 0) {
+        float bv = live ? pv[q].m : -INFINITY;
+        int32_t bi = live ? pv[q].idx : INT32_MAX;
+        if (live)
+          for (int32_t p = sl + lp; p < P.nsplit; p += lp) argmax_merge(bv, bi, rowp[p].m, rowp[p].idx);
+        for (int o = lp >> 1; o > 0; o >>= 1) {
+          const float ov = __shfl_xor(bv, o);
+          const int32_t oi = __shfl_xor(bi, o);
+          argmax_merge(bv, bi, ov, oi);
+        }
+        if (live && sl == 0) {
           L.m[k] = bv;
           L.i[k] = bi;
         }
@@ -1010,7 +1038,7 @@ __global__ __launch_bounds__(kThreads) void k_finish(Params P) {
 struct Plan {
   int32_t spr, nsplit;
   int64_t split_len, chunk_stride;
-  size_t off_parts, off_gz, off_chunks, off_done, total;
+  size_t off_parts, off_rec, off_chunks, off_done, total;
 };
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -1038,8 +1066,8 @@ bool make_plan(int32_t B, int32_t gamma, int64_t V, int dtype, bool greedy, Plan
   // Chunk sums of the stop rows; the element path (one element per unit) has the most chunks.
   pl.chunk_stride = ceil_div(V, kChunkUnits);
   pl.off_parts = 0;
-  pl.off_gz = align_up((size_t)bb * pl.spr * pl.nsplit * sizeof(Partial));
-  pl.off_chunks = pl.off_gz + (greedy ? 0 : align_up((size_t)bb * pl.spr * sizeof(float)));
+  pl.off_rec = align_up((size_t)bb * pl.spr * pl.nsplit * sizeof(Partial));
+  pl.off_chunks = pl.off_rec + align_up((size_t)bb * pl.spr * sizeof(SlotRec));
   pl.off_done = pl.off_chunks +
                 (greedy ? 0 : align_up((size_t)bb * pl.chunk_stride * sizeof(double)));
   pl.total = pl.off_done + align_up((size_t)bb * sizeof(uint32_t));
@@ -1055,15 +1083,16 @@ bool make_plan(int32_t B, int32_t gamma, int64_t V, int dtype, bool greedy, Plan
 // Launch kernel k of the call.  With probe events for it, the dispatch itself records them
 // (hipExtLaunchKernel), so timing adds no marker packets, and no idle time, to the stream.
 template <typename K>
-int launch(K kernel, dim3 grid, const spec_probe *probe, int k, hipStream_t s, Params &P) {
+int launch(K kernel, dim3 grid, int threads, const spec_probe *probe, int k, hipStream_t s,
+           Params &P) {
   hipEvent_t e0 = probe ? static_cast<hipEvent_t>(probe->events[2 * k]) : nullptr;
   hipEvent_t e1 = probe ? static_cast<hipEvent_t>(probe->events[2 * k + 1]) : nullptr;
   if (!e0 && !e1) {
-    kernel<<<grid, dim3(kThreads), 0, s>>>(P);
+    kernel<<<grid, dim3(threads), 0, s>>>(P);
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
   }
   void *args[] = {&P};
-  return hipExtLaunchKernel(reinterpret_cast<const void *>(kernel), grid, dim3(kThreads), args, 0,
+  return hipExtLaunchKernel(reinterpret_cast<const void *>(kernel), grid, dim3(threads), args, 0,
                             s, e0, e1, 0) == hipSuccess
              ? SPEC_OK
              : SPEC_ERR_HIP;
@@ -1084,8 +1113,9 @@ int run(Params P, const Plan &pl, const spec_probe *probe, hipStream_t s) {
   P.nslice = (int32_t)ceil_div(nunits, P.slice_units);
   const uint32_t fy = (uint32_t)(P.B < kMaxGridY ? P.B : kMaxGridY);
   const uint32_t fz = (uint32_t)ceil_div(P.B, fy);
-  SPEC_TRY(launch(k_rowstats<DT, VEC>, dim3((uint32_t)pl.nsplit, gy, gz), probe, 0, s, P));
-  SPEC_TRY(launch(k_finish<DT, VEC>, dim3((uint32_t)P.nslice, fy, fz), probe, 1, s, P));
+  SPEC_TRY(launch(k_rowstats<DT, VEC>, dim3((uint32_t)pl.nsplit, gy, gz), kRsThreads, probe, 0,
+                  s, P));
+  SPEC_TRY(launch(k_finish<DT, VEC>, dim3((uint32_t)P.nslice, fy, fz), kThreads, probe, 1, s, P));
   return SPEC_OK;
 }
 
@@ -1104,7 +1134,7 @@ int setup(Params &P, const Plan &pl, void *workspace, size_t workspace_bytes) {
   if ((int64_t)P.B * pl.spr > kMaxGridY * kMaxGridY) return SPEC_ERR_SHAPE;
   char *ws = static_cast<char *>(workspace);
   P.parts = reinterpret_cast<Partial *>(ws + pl.off_parts);
-  P.gz = reinterpret_cast<float *>(ws + pl.off_gz);
+  P.rec = reinterpret_cast<SlotRec *>(ws + pl.off_rec);
   P.done = reinterpret_cast<uint32_t *>(ws + pl.off_done);
   P.chunk_sums = reinterpret_cast<double *>(ws + pl.off_chunks);
   P.chunk_stride = pl.chunk_stride;
