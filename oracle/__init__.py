@@ -50,6 +50,9 @@ def _load():
         lib.oracle_verify.argtypes = [P, P, ctypes.c_int, P, P, P, ctypes.c_int32,
                                       ctypes.c_int32, P, ctypes.c_int64, P, ctypes.c_int32,
                                       P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int]
+        lib.oracle_commit.restype = ctypes.c_int
+        lib.oracle_commit.argtypes = [P, P, P, ctypes.c_int32, ctypes.c_int32, P,
+                                      ctypes.c_int64, P, P, P]
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -100,6 +103,29 @@ def verify(w, requests: Optional[Sequence[int]] = None, greedy: bool = False,
     if rc != 0:
         raise ValueError(f"oracle_verify rejected its arguments (rc={rc})")
     return out
+
+
+def commit(out_tokens: np.ndarray, num_accepted: np.ndarray, gamma: int, seq_tokens: np.ndarray,
+           seq_len: np.ndarray, cu_draft: Optional[np.ndarray] = None,
+           stats: Optional[np.ndarray] = None, hist: Optional[np.ndarray] = None) -> None:
+    """Commit one step's emitted tokens into the histories ``seq_tokens [B, capacity]``
+    (int32, updated in place with ``seq_len [B]``) and accumulate ``stats`` (uint64[5]:
+    proposed, accepted, emitted, requests, truncated) and ``hist`` (uint64[gamma + 1])."""
+    lib = _load()
+    B = len(num_accepted)
+    for a, dt in ((seq_tokens, np.int32), (seq_len, np.int32)):
+        assert a.dtype == dt and a.flags.c_contiguous
+    for a in (stats, hist):
+        assert a is None or (a.dtype == np.uint64 and a.flags.c_contiguous)
+    if hist is not None:
+        assert len(hist) >= gamma + 1
+    toks = np.ascontiguousarray(out_tokens, dtype=np.int32)
+    nacc = np.ascontiguousarray(num_accepted, dtype=np.int32)
+    cu = None if cu_draft is None else np.ascontiguousarray(cu_draft, dtype=np.int32)
+    rc = lib.oracle_commit(_ptr(toks), _ptr(nacc), _ptr(cu), B, int(gamma), _ptr(seq_tokens),
+                           seq_tokens.shape[1], _ptr(seq_len), _ptr(stats), _ptr(hist))
+    if rc != 0:
+        raise ValueError(f"oracle_commit rejected its arguments (rc={rc})")
 
 
 def tokens_by_request(w, out_tokens: np.ndarray) -> list:

@@ -265,6 +265,56 @@ int oracle_verify(const void *target, const void *draft, int dtype,
   return 0;
 }
 
+/*
+ * After a verification step, commit each request's emitted tokens to its token history and
+ * count what the step did.
+ *
+ * Follows "Accélérer Sonar grâce à la spéculation" (Perplexity) [Inférence avec le décodage
+ * spéculatif; Planification MTP pour un jeton unique]: the accepted length sets the next
+ * sequence length, and instead of a GPU-to-CPU synchronisation a kernel inserts the next
+ * tokens into their slots.  The counters follow "Speculative Decoding : accélérer l'inférence
+ * des LLM" (blent.ai) [Quel gain espérer ?; Mettre en œuvre dans vLLM]: the acceptance rate
+ * and the tokens produced per target pass are the quantities to monitor.
+ *
+ * Readings: request b's history is row b of `seq_tokens` (row stride `capacity`), holding
+ * seq_len[b] tokens.  The step emitted out_tokens[t_b .. t_b + n_b] (n_b accepted drafts, then
+ * the drawn token), t_b = cu_draft[b] + b (dense: b (gamma + 1)).  They are written at
+ * positions seq_len[b] .. seq_len[b] + n_b; positions at or past `capacity` are not written
+ * and count as truncated; the new length is min(seq_len[b] + n_b + 1, capacity).  stats (may
+ * be NULL) accumulates {proposed = sum gamma_b, accepted = sum n_b, emitted = sum (n_b + 1),
+ * requests = B, truncated}; hist (may be NULL, gamma + 1 bins) counts requests by n_b.
+ * Returns 0, or -1 on bad sizes or an accepted count outside [0, gamma_b].
+ */
+int oracle_commit(const int32_t *out_tokens, const int32_t *num_accepted,
+                  const int32_t *cu_draft, int32_t B, int32_t gamma, int32_t *seq_tokens,
+                  int64_t capacity, int32_t *seq_len, uint64_t *stats, uint64_t *hist) {
+  if (B < 0 || gamma < 0 || capacity < 0) return -1;
+  for (int32_t b = 0; b < B; ++b) {
+    int64_t dbase = cu_draft ? cu_draft[b] : (int64_t)b * gamma;
+    int64_t gb = cu_draft ? (int64_t)cu_draft[b + 1] - cu_draft[b] : gamma;
+    int64_t tbase = dbase + b;
+    int64_t n = num_accepted[b];
+    if (gb < 0 || gb > gamma || n < 0 || n > gb) return -1;
+    int64_t len = seq_len[b];
+    uint64_t lost = 0;
+    for (int64_t i = 0; i <= n; ++i) {
+      int64_t pos = len + i;
+      if (pos < capacity) seq_tokens[b * capacity + pos] = out_tokens[tbase + i];
+      else lost++;
+    }
+    seq_len[b] = (int32_t)(len + n + 1 < capacity ? len + n + 1 : capacity);
+    if (stats) {
+      stats[0] += (uint64_t)gb;
+      stats[1] += (uint64_t)n;
+      stats[2] += (uint64_t)(n + 1);
+      stats[3] += 1;
+      stats[4] += lost;
+    }
+    if (hist) hist[n] += 1;
+  }
+  return 0;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

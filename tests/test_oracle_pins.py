@@ -390,3 +390,115 @@ def test_worked_example_tokens_per_pass():
     assert abs(emitted.mean() - closed) < 4 * se, (emitted.mean(), closed, se)
     assert abs(r["num_accepted"].mean() - accepted_closed) < 4 * se
     assert abs(emitted.mean() - g["tokens_per_pass_printed"]) <= g["printed_resolution"]
+
+
+# --------------------------------------------------------------------------- commit step
+
+def _commit_case(B=9, gamma=5, V=300, seed=5, temps=None, capacity=40):
+    temps = np.linspace(0.0, 1.2, B) if temps is None else temps
+    w = workloads.small(B=B, gamma=gamma, V=V, dtype="f32", seed=seed, ragged=True,
+                        temperatures=temps, draft_sigma=0.6)
+    r = oracle.verify(w)
+    rng = np.random.default_rng(seed)
+    seq = rng.integers(0, V, size=(B, capacity)).astype(np.int32)
+    length = rng.integers(0, capacity - gamma - 1, size=B).astype(np.int32)
+    return w, r, seq, length
+
+
+def test_commit_appends_accepted_drafts_then_the_emitted_token():
+    # The accepted prefix is the drafts themselves (aimpact, "Il meccanismo"), followed by
+    # the one token drawn at the stop row; the rest of each history is untouched.
+    w, r, seq, length = _commit_case()
+    before, len0 = seq.copy(), length.copy()
+    oracle.commit(r["out_tokens"], r["num_accepted"], w.gamma, seq, length, cu_draft=w.cu_draft)
+    for b in range(w.B):
+        n = int(r["num_accepted"][b])
+        drafts = w.draft_tokens[w.draft_base[b]: w.draft_base[b] + n]
+        L = int(len0[b])
+        assert length[b] == L + n + 1
+        np.testing.assert_array_equal(seq[b, L: L + n], drafts)
+        assert seq[b, L + n] == r["out_tokens"][w.target_base[b] + n]
+        np.testing.assert_array_equal(seq[b, :L], before[b, :L])
+        np.testing.assert_array_equal(seq[b, L + n + 1:], before[b, L + n + 1:])
+
+
+def test_commit_of_a_greedy_step_appends_target_argmax_decoding():
+    # At temperature zero the committed tokens are the target's own argmax decoding up to the
+    # first disagreement, computed here with numpy (first occurrence on ties).
+    w, r, seq, length = _commit_case(temps=np.zeros(9), seed=8)
+    len0 = length.copy()
+    oracle.commit(r["out_tokens"], r["num_accepted"], w.gamma, seq, length, cu_draft=w.cu_draft)
+    zt = workloads.decode(w.target, w.dtype)
+    for b in range(w.B):
+        t0, d0, gb = w.target_base[b], w.draft_base[b], int(w.gammas[b])
+        ref = []
+        for i in range(gb + 1):
+            g = int(np.argmax(zt[t0 + i]))
+            ref.append(g)
+            if i == gb or w.draft_tokens[d0 + i] != g:
+                break
+        L = int(len0[b])
+        assert length[b] == L + len(ref)
+        np.testing.assert_array_equal(seq[b, L: L + len(ref)], ref)
+
+
+def test_commit_truncates_at_capacity_and_never_writes_past_it():
+    w, r, seq, length = _commit_case(B=7, gamma=6, seed=11, capacity=12)
+    length[:] = np.array([12, 11, 10, 8, 5, 0, 12], dtype=np.int32)[: w.B]
+    before, len0 = seq.copy(), length.copy()
+    stats = np.zeros(5, dtype=np.uint64)
+    oracle.commit(r["out_tokens"], r["num_accepted"], w.gamma, seq, length,
+                  cu_draft=w.cu_draft, stats=stats)
+    lost = 0
+    for b in range(w.B):
+        n = int(r["num_accepted"][b])
+        L = int(len0[b])
+        assert length[b] == min(L + n + 1, 12)
+        lost += max(0, L + n + 1 - 12)
+        np.testing.assert_array_equal(seq[b, :L], before[b, :L])
+    assert int(stats[4]) == lost
+    assert int(stats[2]) == int(r["num_accepted"].sum()) + w.B
+
+
+def test_commit_counters_accumulate_and_match_the_step():
+    w, r, seq, length = _commit_case(seed=21)
+    stats = np.zeros(5, dtype=np.uint64)
+    hist = np.zeros(w.gamma + 1, dtype=np.uint64)
+    for _ in range(2):
+        s2, l2 = seq.copy(), length.copy()
+        oracle.commit(r["out_tokens"], r["num_accepted"], w.gamma, s2, l2,
+                      cu_draft=w.cu_draft, stats=stats, hist=hist)
+    n = r["num_accepted"].astype(np.int64)
+    assert list(stats[:4]) == [2 * int(w.gammas.sum()), 2 * int(n.sum()),
+                               2 * int(n.sum() + w.B), 2 * w.B]
+    np.testing.assert_array_equal(hist, 2 * np.bincount(n, minlength=w.gamma + 1))
+
+
+def test_commit_telemetry_reproduces_the_worked_example():
+    # blent.ai, "Quel gain espérer ?": at acceptance rate 0.8 and 4 drafts the target pass
+    # yields (1 - 0.8^5) / 0.2 = 3.36 (printed: about 3.4) tokens on average; the counters
+    # must show it, and the accepted lengths must follow P(n = k) = a^k (1 - a) for k < 4,
+    # P(n = 4) = a^4 (i.i.d. acceptance at rate a).
+    g = json.loads((GOLDEN / "tokens_per_pass.json").read_text())
+    alpha, gamma = g["alpha"], g["gamma"]
+    zt = np.log(np.array([[0.9, 0.1]] * (gamma + 1)))
+    zd = np.log(np.array([[0.7, 0.3]] * gamma))
+    n = 200_000
+    w = workloads.tiled(zt, zd, n, T=1.0, seed=41)
+    r = oracle.verify(w)
+    seq = np.zeros((n, gamma + 1), dtype=np.int32)
+    length = np.zeros(n, dtype=np.int32)
+    stats = np.zeros(5, dtype=np.uint64)
+    hist = np.zeros(gamma + 1, dtype=np.uint64)
+    oracle.commit(r["out_tokens"], r["num_accepted"], gamma, seq, length, stats=stats, hist=hist)
+    proposed, accepted, emitted, requests, lost = (int(v) for v in stats)
+    assert (proposed, requests, lost) == (gamma * n, n, 0)
+    per_pass = emitted / requests
+    closed = (1 - alpha ** (gamma + 1)) / (1 - alpha)
+    assert abs(per_pass - closed) < 4 * 1.25 / np.sqrt(n)
+    assert abs(per_pass - g["tokens_per_pass_printed"]) <= g["printed_resolution"]
+    law = np.array([alpha ** k * (1 - alpha) for k in range(gamma)] + [alpha ** gamma])
+    pval, x2, df = chi2_pvalue(hist.astype(np.int64), law)
+    assert pval > 1e-3, (pval, x2, df)
+    assert accepted / proposed == pytest.approx(sum(alpha ** k for k in range(1, gamma + 1)) / gamma,
+                                                abs=4 * 1.4 / gamma / np.sqrt(n))
