@@ -136,6 +136,39 @@ int spec_verify_greedy(const void *target_logits, int dtype, const int32_t *draf
                        int32_t *out_tokens, int32_t *out_num_accepted, void *workspace,
                        size_t workspace_bytes, const spec_probe *probe, void *stream);
 
+/*
+ * spec_verify_commit — hand a verification step's result to the next step on the device.
+ *
+ * "Accélérer Sonar grâce à la spéculation" (Perplexity), sections "Inférence avec le
+ * décodage spéculatif" and "Planification MTP pour un jeton unique": the accepted length sets
+ * the next sequence length, and a kernel that inserts the new tokens into their slots spares
+ * the GPU-to-CPU synchronisation.  "Speculative Decoding : accélérer l'inférence des LLM"
+ * (blent.ai), sections "Quel gain espérer ?" and "Mettre en œuvre dans vLLM": the acceptance
+ * rate and the tokens per target pass are what to monitor.
+ *
+ *  out_tokens, out_num_accepted, cu_draft, B, gamma
+ *                 a spec_verify_sample / spec_verify_greedy call's outputs and layout
+ *  seq_tokens     [B, capacity] int32, row b = request b's token history (row stride capacity)
+ *  seq_len        [B] int32, tokens held per row; read and updated
+ *  stats          NULL, or uint64[5] accumulated (atomically) with {proposed = sum gamma_b,
+ *                 accepted = sum n_b, emitted = sum (n_b + 1), requests = B, truncated};
+ *                 zero it to start.  Acceptance rate = accepted / proposed, tokens per pass =
+ *                 emitted / requests.
+ *  accept_hist    NULL, or uint64[gamma + 1] accumulated: requests per accepted count n_b
+ *  stream         hipStream_t; ordered after the verification call on the same stream
+ *
+ * Request b's n_b + 1 emitted tokens (slots cu_draft[b] + b .. + n_b of out_tokens) are written
+ * to seq_tokens[b][seq_len[b] ..]; those at or past `capacity` are dropped and counted as
+ * truncated; seq_len[b] becomes min(seq_len[b] + n_b + 1, capacity).  All pointers are device
+ * pointers.  Errors: SPEC_ERR_SHAPE (B < 0, gamma outside [0, 64], capacity < 0), SPEC_ERR_NULL,
+ * SPEC_ERR_HIP; B == 0 enqueues nothing.  Device data are not checked: n_b is clamped to
+ * [0, gamma_b] and seq_len[b] to [0, capacity] for memory safety only.
+ */
+int spec_verify_commit(const int32_t *out_tokens, const int32_t *out_num_accepted,
+                       const int32_t *cu_draft, int32_t B, int32_t gamma, int32_t *seq_tokens,
+                       int64_t capacity, int32_t *seq_len, uint64_t *stats,
+                       uint64_t *accept_hist, void *stream);
+
 /* Workspace bytes needed by either entry point for these sizes; 0 for invalid sizes. */
 size_t spec_verify_workspace_size(int32_t B, int32_t gamma, int64_t V, int dtype);
 

@@ -50,6 +50,8 @@ def lib():
         L.spec_verify_greedy.restype = ctypes.c_int
         L.spec_verify_greedy.argtypes = [P, ctypes.c_int, P, i32, i32, P, i64, P, P, P, sz, P,
                                          P]
+        L.spec_verify_commit.restype = ctypes.c_int
+        L.spec_verify_commit.argtypes = [P, P, P, i32, i32, P, i64, P, P, P, P]
         L.spec_verify_workspace_size.restype = sz
         L.spec_verify_workspace_size.argtypes = [i32, i32, i64, ctypes.c_int]
         L.spec_verify_strerror.restype = ctypes.c_char_p
@@ -181,6 +183,27 @@ def spec_verify_greedy(target_logits, draft_tokens, gamma: int, out_tokens,
     args = _greedy_args(target_logits, draft_tokens, gamma, out_tokens, out_num_accepted,
                         workspace, cu_draft, probe, stream)
     _check(lib().spec_verify_greedy(*args), "spec_verify_greedy")
+
+
+def spec_verify_commit(out_tokens, out_num_accepted, gamma: int, seq_tokens, seq_len,
+                       cu_draft=None, stats=None, accept_hist=None, stream=None) -> None:
+    """Append a verification step's emitted tokens to the histories ``seq_tokens [B, cap]``
+    (int32) at ``seq_len [B]`` (int32, updated), on the device; ``stats`` (int64 tensor of 5,
+    read as uint64) and ``accept_hist`` (int64 tensor of gamma + 1) accumulate the step's
+    counters.  ``B`` is ``out_num_accepted.numel()``."""
+    torch = _torch()
+    B = out_num_accepted.numel()
+    if seq_tokens.dim() != 2 or seq_tokens.shape[0] < B:
+        raise ValueError("seq_tokens must be [B, capacity]")
+    rc = lib().spec_verify_commit(
+        _dev(out_tokens, "out_tokens", torch.int32),
+        _dev(out_num_accepted, "out_num_accepted", torch.int32, B),
+        _dev(cu_draft, "cu_draft", torch.int32, B + 1), B, int(gamma),
+        _dev(seq_tokens, "seq_tokens", torch.int32), seq_tokens.shape[1],
+        _dev(seq_len, "seq_len", torch.int32, B),
+        _dev(stats, "stats", torch.int64, 5),
+        _dev(accept_hist, "accept_hist", torch.int64, int(gamma) + 1), _stream(stream))
+    _check(rc, "spec_verify_commit")
 
 
 class PreparedCall:

@@ -1033,6 +1033,77 @@ __global__ __launch_bounds__(kThreads) void k_finish(Params P) {
   draw_token<DT, VEC, kThreads>(P, b, st, cs, D);
 }
 
+// ------------------------------------------------------------------ k_commit
+
+struct CommitParams {
+  const int32_t *out_tokens, *out_n, *cu;
+  int32_t B, gamma;
+  int32_t *seq;
+  int64_t capacity;
+  int32_t *seq_len;
+  unsigned long long *stats, *hist;
+};
+
+// One thread per request: append the request's n_b + 1 emitted tokens to its history at
+// seq_len[b], clamp the length at capacity, and fold the step into the counters (wavefront
+// sums and an LDS histogram, then one device atomic per counter and bin per workgroup).
+__global__ __launch_bounds__(kThreads) void k_commit(CommitParams C) {
+  __shared__ unsigned long long s_sum[5][kWaves];
+  __shared__ uint32_t s_hist[SPEC_MAX_GAMMA + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (C.hist)
+    for (int i = tid; i <= C.gamma; i += kThreads) s_hist[i] = 0u;
+  __syncthreads();
+  const int64_t b = (int64_t)blockIdx.x * kThreads + tid;
+  unsigned long long v[5] = {0, 0, 0, 0, 0};
+  if (b < C.B) {
+    int64_t dbase, gb;
+    if (C.cu) {
+      dbase = C.cu[b];
+      gb = (int64_t)C.cu[b + 1] - dbase;
+    } else {
+      dbase = b * C.gamma;
+      gb = C.gamma;
+    }
+    // memory safety on device data the host cannot check
+    gb = gb < 0 ? 0 : (gb > C.gamma ? C.gamma : gb);
+    int64_t n = C.out_n[b];
+    n = n < 0 ? 0 : (n > gb ? gb : n);
+    int64_t len = C.seq_len[b];
+    len = len < 0 ? 0 : (len > C.capacity ? C.capacity : len);
+    const int32_t *src = C.out_tokens + dbase + b;
+    int32_t *dst = C.seq + b * C.capacity;
+    for (int64_t i = 0; i <= n; ++i)
+      if (len + i < C.capacity) dst[len + i] = src[i];
+    const int64_t end = len + n + 1;
+    C.seq_len[b] = (int32_t)(end < C.capacity ? end : C.capacity);
+    v[0] = (unsigned long long)gb;
+    v[1] = (unsigned long long)n;
+    v[2] = (unsigned long long)(n + 1);
+    v[3] = 1ull;
+    v[4] = (unsigned long long)(end > C.capacity ? end - C.capacity : 0);
+    if (C.hist) atomicAdd(&s_hist[n], 1u);
+  }
+  if (C.stats) {
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      unsigned long long x = v[k];
+      for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+      if (lane == 0) s_sum[k][wave] = x;
+    }
+  }
+  __syncthreads();
+  if (C.stats && tid < 5) {
+    unsigned long long x = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) x += s_sum[tid][w];
+    if (x) atomicAdd(&C.stats[tid], x);
+  }
+  if (C.hist)
+    for (int i = tid; i <= C.gamma; i += kThreads)
+      if (s_hist[i]) atomicAdd(&C.hist[i], (unsigned long long)s_hist[i]);
+}
+
 // ------------------------------------------------------------------ host side
 
 struct Plan {
@@ -1243,6 +1314,30 @@ int spec_verify_greedy(const void *target_logits, int dtype, const int32_t *draf
   hipStream_t s = static_cast<hipStream_t>(stream);
   return dtype == SPEC_F32 ? dispatch<SPEC_F32>(P, pl, probe, s, vec)
                            : dispatch<SPEC_BF16>(P, pl, probe, s, vec);
+}
+
+int spec_verify_commit(const int32_t *out_tokens, const int32_t *out_num_accepted,
+                       const int32_t *cu_draft, int32_t B, int32_t gamma, int32_t *seq_tokens,
+                       int64_t capacity, int32_t *seq_len, uint64_t *stats,
+                       uint64_t *accept_hist, void *stream) {
+  if (B < 0 || gamma < 0 || gamma > SPEC_MAX_GAMMA || capacity < 0) return SPEC_ERR_SHAPE;
+  if (B == 0) return SPEC_OK;
+  if (!out_tokens || !out_num_accepted || !seq_tokens || !seq_len) return SPEC_ERR_NULL;
+  if ((int64_t)B > (int64_t)INT32_MAX - kThreads) return SPEC_ERR_SHAPE;
+  CommitParams C = {};
+  C.out_tokens = out_tokens;
+  C.out_n = out_num_accepted;
+  C.cu = cu_draft;
+  C.B = B;
+  C.gamma = gamma;
+  C.seq = seq_tokens;
+  C.capacity = capacity;
+  C.seq_len = seq_len;
+  C.stats = reinterpret_cast<unsigned long long *>(stats);
+  C.hist = reinterpret_cast<unsigned long long *>(accept_hist);
+  k_commit<<<dim3((uint32_t)ceil_div(B, kThreads)), dim3(kThreads), 0,
+             static_cast<hipStream_t>(stream)>>>(C);
+  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
 }  // extern "C"

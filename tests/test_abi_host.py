@@ -22,8 +22,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert names == ["spec_verify_greedy", "spec_verify_sample", "spec_verify_strerror",
-                     "spec_verify_workspace_size"]
+    assert names == ["spec_verify_commit", "spec_verify_greedy", "spec_verify_sample",
+                     "spec_verify_strerror", "spec_verify_workspace_size"]
     lib = sv.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -90,3 +90,24 @@ def test_empty_batch_is_a_no_op():
 def test_workspace_one_byte_short_is_refused():
     need = sv.spec_verify_workspace_size(2, 3, 1000, 0)
     assert _sample(wsb=need - 1) == -4
+
+
+def _commit(**kw):
+    a = dict(out=FAKE, n=FAKE, cu=None, B=2, gamma=3, seq=FAKE, cap=16, seq_len=FAKE,
+             stats=None, hist=None, stream=None)
+    a.update(kw)
+    return sv.lib().spec_verify_commit(a["out"], a["n"], a["cu"], a["B"], a["gamma"], a["seq"],
+                                       a["cap"], a["seq_len"], a["stats"], a["hist"],
+                                       a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), -2), (dict(gamma=65), -2), (dict(gamma=-1), -2), (dict(cap=-1), -2),
+    (dict(out=None), -1), (dict(n=None), -1), (dict(seq=None), -1), (dict(seq_len=None), -1),
+])
+def test_commit_rejects_bad_arguments_before_launching(kw, code):
+    assert _commit(**kw) == code
+
+
+def test_commit_with_no_requests_is_a_no_op():
+    assert _commit(B=0, out=None, n=None, seq=None, seq_len=None) == 0

@@ -305,6 +305,71 @@ def test_prepared_call_repeats_the_entry_point():
     np.testing.assert_array_equal(nacc.cpu().numpy(), refg["num_accepted"])
 
 
+@pytest.mark.parametrize("capacity,fill", [(64, "low"), (14, "high")])
+def test_commit_matches_oracle(capacity, fill):
+    # the GPU commit of a verification step's outputs against the oracle's commit of the
+    # same outputs (histories and counters bit-exact)
+    import torch
+    import speculative_sampling_verification_spec_amd as sv
+    B, gamma = 300, 6
+    temps = np.where(np.arange(B) % 4 == 0, 0.0, np.linspace(0.3, 1.3, B))
+    w = workloads.small(B=B, gamma=gamma, V=5000, dtype="bf16", seed=capacity, ragged=True,
+                        temperatures=temps, draft_sigma=0.7)
+    o = oracle.verify(w)   # both commits take the oracle's step as input
+    rng = np.random.default_rng(capacity)
+    hi = capacity if fill == "high" else capacity - gamma - 1
+    seq0 = rng.integers(0, 5000, size=(B, capacity)).astype(np.int32)
+    len0 = rng.integers(0, hi + 1, size=B).astype(np.int32)
+    seq_o, len_o = seq0.copy(), len0.copy()
+    st_o = np.zeros(5, dtype=np.uint64)
+    hi_o = np.zeros(gamma + 1, dtype=np.uint64)
+    for _ in range(2):   # the counters accumulate; the histories take the second step too
+        oracle.commit(o["out_tokens"], o["num_accepted"], gamma, seq_o, len_o,
+                      cu_draft=w.cu_draft, stats=st_o, hist=hi_o)
+    dev = dict(out=torch.from_numpy(o["out_tokens"]).cuda(),
+               n=torch.from_numpy(o["num_accepted"]).cuda(),
+               cu=torch.from_numpy(w.cu_draft.astype(np.int32)).cuda(),
+               seq=torch.from_numpy(seq0).cuda(), len=torch.from_numpy(len0).cuda(),
+               st=torch.zeros(5, dtype=torch.int64, device="cuda"),
+               hi=torch.zeros(gamma + 1, dtype=torch.int64, device="cuda"))
+    for _ in range(2):
+        sv.spec_verify_commit(dev["out"], dev["n"], gamma, dev["seq"], dev["len"],
+                              cu_draft=dev["cu"], stats=dev["st"], accept_hist=dev["hi"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dev["seq"].cpu().numpy(), seq_o)
+    np.testing.assert_array_equal(dev["len"].cpu().numpy(), len_o)
+    np.testing.assert_array_equal(dev["st"].cpu().numpy().view(np.uint64), st_o)
+    np.testing.assert_array_equal(dev["hi"].cpu().numpy().view(np.uint64), hi_o)
+    if fill == "high":
+        assert int(st_o[4]) > 0   # the truncation path ran
+
+
+def test_commit_dense_layout_and_many_requests():
+    import torch
+    import speculative_sampling_verification_spec_amd as sv
+    B, gamma, cap = 5000, 3, 9
+    rng = np.random.default_rng(7)
+    n = rng.integers(0, gamma + 1, size=B).astype(np.int32)
+    out = rng.integers(0, 1000, size=B * (gamma + 1)).astype(np.int32)
+    seq0 = np.full((B, cap), -5, dtype=np.int32)
+    len0 = rng.integers(0, cap + 1, size=B).astype(np.int32)
+    seq_o, len_o = seq0.copy(), len0.copy()
+    st_o = np.zeros(5, dtype=np.uint64)
+    hi_o = np.zeros(gamma + 1, dtype=np.uint64)
+    oracle.commit(out, n, gamma, seq_o, len_o, stats=st_o, hist=hi_o)
+    seq = torch.from_numpy(seq0).cuda()
+    ln = torch.from_numpy(len0).cuda()
+    st = torch.zeros(5, dtype=torch.int64, device="cuda")
+    hi = torch.zeros(gamma + 1, dtype=torch.int64, device="cuda")
+    sv.spec_verify_commit(torch.from_numpy(out).cuda(), torch.from_numpy(n).cuda(), gamma, seq,
+                          ln, stats=st, accept_hist=hi)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(seq.cpu().numpy(), seq_o)
+    np.testing.assert_array_equal(ln.cpu().numpy(), len_o)
+    np.testing.assert_array_equal(st.cpu().numpy().view(np.uint64), st_o)
+    np.testing.assert_array_equal(hi.cpu().numpy().view(np.uint64), hi_o)
+
+
 # ----------------------------------------------------------------------- distribution
 
 def test_gpu_chi_square_emitted_tokens_follow_p():
