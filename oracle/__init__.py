@@ -53,6 +53,9 @@ def _load():
         lib.oracle_commit.restype = ctypes.c_int
         lib.oracle_commit.argtypes = [P, P, P, ctypes.c_int32, ctypes.c_int32, P,
                                       ctypes.c_int64, P, P, P]
+        lib.oracle_ngram.restype = ctypes.c_int
+        lib.oracle_ngram.argtypes = [P, ctypes.c_int64, P, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P]
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -126,6 +129,28 @@ def commit(out_tokens: np.ndarray, num_accepted: np.ndarray, gamma: int, seq_tok
                            seq_tokens.shape[1], _ptr(seq_len), _ptr(stats), _ptr(hist))
     if rc != 0:
         raise ValueError(f"oracle_commit rejected its arguments (rc={rc})")
+
+
+def ngram(seq_tokens: np.ndarray, seq_len: np.ndarray, n_min: int, n_max: int,
+          gamma: int) -> dict:
+    """Prompt-lookup proposals for every request's context ``seq_tokens[b, :seq_len[b]]``:
+    counts, dense [B, gamma] (-1 padded), cu [B + 1], packed [sum counts], match_j, match_n."""
+    lib = _load()
+    seq = np.ascontiguousarray(seq_tokens, dtype=np.int32)
+    ln = np.ascontiguousarray(seq_len, dtype=np.int32)
+    B, cap = seq.shape
+    out = dict(counts=np.full(B, -2, dtype=np.int32),
+               dense=np.full((B, gamma), -2, dtype=np.int32),
+               cu=np.full(B + 1, -2, dtype=np.int32),
+               packed=np.full(max(B * gamma, 1), -2, dtype=np.int32),
+               match_j=np.full(B, -2, dtype=np.int32), match_n=np.full(B, -2, dtype=np.int32))
+    rc = lib.oracle_ngram(_ptr(seq), cap, _ptr(ln), B, int(n_min), int(n_max), int(gamma),
+                          _ptr(out["counts"]), _ptr(out["dense"]), _ptr(out["cu"]),
+                          _ptr(out["packed"]), _ptr(out["match_j"]), _ptr(out["match_n"]))
+    if rc != 0:
+        raise ValueError(f"oracle_ngram rejected its arguments (rc={rc})")
+    out["packed"] = out["packed"][: int(out["cu"][-1])]
+    return out
 
 
 def tokens_by_request(w, out_tokens: np.ndarray) -> list:

@@ -315,6 +315,69 @@ int oracle_commit(const int32_t *out_tokens, const int32_t *num_accepted,
   return 0;
 }
 
+/*
+ * N-gram (prompt lookup) drafting for the next step.
+ *
+ * Follows "Speculative Decoding : accélérer l'inférence des LLM" (blent.ai) [N-gram lookup et
+ * variantes sans modèle; Mettre en œuvre dans vLLM]: the last n generated tokens are looked
+ * up in the context and the tokens that followed them there are proposed as drafts, with n
+ * bounded by prompt_lookup_min and prompt_lookup_max; no model is involved.
+ *
+ * Readings (the page leaves them open): request b's context is h = seq_tokens[b][0 .. L),
+ * L = seq_len[b].  n runs from n_max down to n_min (longest first), n < L; the pattern is the
+ * suffix h[L-n .. L); the occurrence used is the earliest j in [0, L - n) with
+ * h[j .. j+n) == h[L-n .. L) (a proper earlier occurrence; it may overlap the suffix); the
+ * proposals are h[j+n .. min(j+n+gamma, L)), at least one token.  The first n with an
+ * occurrence decides; with none, the request gets no proposals.
+ * Outputs: counts[b]; dense[b][0 .. gamma) (proposals then -1); when cu is not NULL,
+ * cu[0..B] = prefix sums of counts and packed[cu[b] ..] = request b's proposals (the draft
+ * layout of the verification step); match_j / match_n (may be NULL): j and n, or -1 and 0.
+ * Returns 0, or -1 on bad sizes.
+ */
+int oracle_ngram(const int32_t *seq_tokens, int64_t capacity, const int32_t *seq_len,
+                 int32_t B, int32_t n_min, int32_t n_max, int32_t gamma, int32_t *counts,
+                 int32_t *dense, int32_t *cu, int32_t *packed, int32_t *match_j,
+                 int32_t *match_n) {
+  if (B < 0 || capacity < 0 || n_min < 1 || n_max < n_min || gamma < 0) return -1;
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t *h = seq_tokens + (int64_t)b * capacity;
+    int64_t L = seq_len[b];
+    if (L < 0) L = 0;
+    if (L > capacity) L = capacity;
+    int64_t found_j = -1, found_n = 0;
+    for (int64_t n = n_max; n >= n_min && found_j < 0; --n) {
+      if (n >= L) continue;
+      for (int64_t j = 0; j < L - n; ++j) {
+        int64_t k = 0;
+        while (k < n && h[j + k] == h[L - n + k]) ++k;
+        if (k == n) {
+          found_j = j;
+          found_n = n;
+          break;
+        }
+      }
+    }
+    int64_t cnt = 0;
+    if (found_j >= 0) {
+      int64_t start = found_j + found_n;
+      cnt = L - start < gamma ? L - start : gamma;
+    }
+    counts[b] = (int32_t)cnt;
+    for (int64_t i = 0; i < gamma; ++i)
+      dense[(int64_t)b * gamma + i] = i < cnt ? h[found_j + found_n + i] : -1;
+    if (match_j) match_j[b] = (int32_t)found_j;
+    if (match_n) match_n[b] = (int32_t)found_n;
+  }
+  if (cu) {
+    cu[0] = 0;
+    for (int32_t b = 0; b < B; ++b) cu[b + 1] = cu[b] + counts[b];
+    if (packed)
+      for (int32_t b = 0; b < B; ++b)
+        for (int32_t i = 0; i < counts[b]; ++i) packed[cu[b] + i] = dense[(int64_t)b * gamma + i];
+  }
+  return 0;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

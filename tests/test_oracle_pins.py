@@ -502,3 +502,85 @@ def test_commit_telemetry_reproduces_the_worked_example():
     assert pval > 1e-3, (pval, x2, df)
     assert accepted / proposed == pytest.approx(sum(alpha ** k for k in range(1, gamma + 1)) / gamma,
                                                 abs=4 * 1.4 / gamma / np.sqrt(n))
+
+
+# --------------------------------------------------------------------------- n-gram drafter
+
+def _find_reference(h, n_min, n_max, gamma):
+    """Prompt lookup through Python's substring search (lowest index): tokens become
+    fixed-width text, the pattern is the last n tokens, searched in the context without its
+    last token (so only proper earlier occurrences, possibly overlapping the suffix)."""
+    L = len(h)
+    text = "".join(f"|{t:08x}" for t in h[: max(L - 1, 0)])
+    for n in range(n_max, n_min - 1, -1):
+        if n >= L:
+            continue
+        pat = "".join(f"|{t:08x}" for t in h[L - n:])
+        pos = text.find(pat)
+        if pos >= 0:
+            j = pos // 9
+            return list(h[j + n: min(j + n + gamma, L)]), j, n
+    return [], -1, 0
+
+
+def _ngram_one(h, n_min, n_max, gamma, capacity=None):
+    cap = capacity or max(len(h), 1)
+    seq = np.zeros((1, cap), dtype=np.int32)
+    seq[0, : len(h)] = h
+    return oracle.ngram(seq, np.array([len(h)], dtype=np.int32), n_min, n_max, gamma)
+
+
+@pytest.mark.parametrize("h,n_min,n_max,gamma,expect", [
+    ([1, 2, 3, 9, 1, 2, 3], 1, 3, 2, [9, 1]),        # the 3-gram 1 2 3 seen at 0
+    ([5, 8, 6, 7, 2, 6, 7], 1, 2, 3, [2, 6, 7]),     # longest first: 2-gram 6 7 beats 1-gram 7
+    ([1, 2, 3, 4], 1, 3, 4, []),                     # nothing recurs
+    ([4, 4], 1, 1, 5, [4]),                          # proposals stop at the context's end
+    ([7, 7, 7, 7], 1, 3, 4, [7]),                    # overlapping occurrence at 0
+    ([3, 1, 3, 2, 3], 1, 1, 2, [1, 3]),              # earliest of several occurrences
+    ([9], 1, 4, 3, []),                              # too short to hold any earlier n-gram
+    ([2, 5, 2, 5, 2], 2, 2, 1, [5]),                 # n fixed at 2: 5 2 at 1, then 5
+])
+def test_ngram_hand_cases(h, n_min, n_max, gamma, expect):
+    r = _ngram_one(h, n_min, n_max, gamma)
+    assert r["counts"][0] == len(expect)
+    assert list(r["dense"][0, : len(expect)]) == expect
+    assert all(v == -1 for v in r["dense"][0, len(expect):])
+    assert list(r["packed"]) == expect and list(r["cu"]) == [0, len(expect)]
+
+
+@pytest.mark.parametrize("alphabet", [2, 3, 8, 50])
+def test_ngram_matches_substring_search(alphabet):
+    rng = np.random.default_rng(alphabet)
+    B, cap, gamma = 200, 80, 5
+    seq = rng.integers(0, alphabet, size=(B, cap)).astype(np.int32)
+    length = rng.integers(0, cap + 1, size=B).astype(np.int32)
+    for n_min, n_max in ((1, 1), (2, 4), (1, 6)):
+        r = oracle.ngram(seq, length, n_min, n_max, gamma)
+        off = 0
+        assert r["cu"][0] == 0
+        for b in range(B):
+            h = list(seq[b, : length[b]])
+            ref, j, n = _find_reference(h, n_min, n_max, gamma)
+            assert list(r["dense"][b, : r["counts"][b]]) == ref
+            assert (r["match_j"][b], r["match_n"][b]) == (j, n)
+            assert r["cu"][b + 1] - r["cu"][b] == len(ref)
+            assert list(r["packed"][off: off + len(ref)]) == ref
+            off += len(ref)
+
+
+def test_ngram_proposals_continue_the_matched_window():
+    # invariants: the matched window equals the pattern, the proposals are what followed it
+    rng = np.random.default_rng(3)
+    B, cap, gamma = 100, 200, 7
+    base = rng.integers(0, 1000, size=(B, cap)).astype(np.int32)
+    for b in range(B):   # plant a copy of an earlier span at the end of the context
+        a = rng.integers(0, 60)
+        base[b, 150:170] = base[b, a: a + 20]
+    length = np.full(B, 170, dtype=np.int32)
+    r = oracle.ngram(base, length, 2, 5, gamma)
+    assert (r["match_n"] == 5).all()
+    for b in range(B):
+        j, n, c = r["match_j"][b], r["match_n"][b], r["counts"][b]
+        assert c == min(gamma, 170 - (j + n)) and c >= 1
+        np.testing.assert_array_equal(base[b, j: j + n], base[b, 170 - n: 170])
+        np.testing.assert_array_equal(r["dense"][b, :c], base[b, j + n: j + n + c])
