@@ -243,9 +243,33 @@ def main():
                      "traffic": None if traffic is None else traffic["hbm_bytes_per_launch"]},
         "cpu_baseline": None,
     }
+    result["commit"] = time_commit(sv, w, out, nacc, d=inputs[0], steps=args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def time_commit(sv, w, out, nacc, d, steps):
+    """spec_verify_commit on the last step's outputs: append to histories with room for
+    every step timed, and count; not part of ``value`` (the step of the verification)."""
+    import torch
+    cap = (steps + 2) * (w.gamma + 1)
+    seq = torch.zeros((w.B, cap), dtype=torch.int32, device="cuda")
+    ln = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+    stats = torch.zeros(5, dtype=torch.int64, device="cuda")
+    hist = torch.zeros(w.gamma + 1, dtype=torch.int64, device="cuda")
+    call = lambda: sv.spec_verify_commit(out, nacc, w.gamma, seq, ln, cu_draft=d["cu"],
+                                         stats=stats, accept_hist=hist)
+    call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) * 1e6 / steps
+    st = stats.cpu().numpy()
+    return {"us_per_call": round(us, 2), "acceptance_rate": round(float(st[1] / max(st[0], 1)), 4),
+            "tokens_per_pass": round(float(st[2] / max(st[3], 1)), 4)}
 
 
 if __name__ == "__main__":

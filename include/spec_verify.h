@@ -169,6 +169,45 @@ int spec_verify_commit(const int32_t *out_tokens, const int32_t *out_num_accepte
                        int64_t capacity, int32_t *seq_len, uint64_t *stats,
                        uint64_t *accept_hist, void *stream);
 
+/* Longest n-gram spec_ngram_propose looks up. */
+#define SPEC_NGRAM_MAX_N 64
+
+/*
+ * spec_ngram_propose — draft tokens for the next step by n-gram (prompt) lookup.
+ *
+ * "Speculative Decoding : accélérer l'inférence des LLM" (blent.ai), sections "N-gram lookup et
+ * variantes sans modèle" and "Mettre en œuvre dans vLLM": the last n generated tokens are
+ * looked up in the context and the tokens that followed them are proposed, with n between
+ * prompt_lookup_min and prompt_lookup_max; no draft model.
+ *
+ * Conventions where the page leaves them open: request b's context is
+ * seq_tokens[b][0 .. L), L = seq_len[b] (clamped to [0, capacity]); n runs from n_max down to
+ * n_min, n < L; the pattern is the last n tokens; the occurrence used is the earliest start j
+ * in [0, L - n) (a proper earlier occurrence, possibly overlapping the pattern); the
+ * proposals are the up to gamma tokens from j + n on, stopping at L.  No occurrence for any n:
+ * no proposals (a verification with gamma_b = 0 still emits one token).
+ *
+ *  seq_tokens   [B, capacity] int32      contexts, row stride capacity (spec_verify_commit's
+ *                                        layout)
+ *  seq_len      [B] int32
+ *  n_min, n_max 1 <= n_min <= n_max <= SPEC_NGRAM_MAX_N
+ *  gamma        proposals at most, 0..SPEC_MAX_GAMMA
+ *  out_counts   [B] int32                proposals per request
+ *  out_dense    [B, gamma] int32         proposals, then -1
+ *  out_cu       [B + 1] int32 or NULL    prefix sums of out_counts (cu_draft of the
+ *                                        verification step)
+ *  out_packed   [B * gamma] int32 or NULL  proposals packed at out_cu[b] (draft_tokens of the
+ *                                        verification step); NULL exactly when out_cu is
+ *                                        (with gamma == 0, out_dense and out_packed may be NULL)
+ *
+ * All pointers are device pointers; asynchronous on `stream` (one launch, two with out_cu).
+ * Errors: SPEC_ERR_SHAPE, SPEC_ERR_NULL, SPEC_ERR_HIP; B == 0 enqueues nothing.
+ */
+int spec_ngram_propose(const int32_t *seq_tokens, int64_t capacity, const int32_t *seq_len,
+                       int32_t B, int32_t n_min, int32_t n_max, int32_t gamma,
+                       int32_t *out_counts, int32_t *out_dense, int32_t *out_cu,
+                       int32_t *out_packed, void *stream);
+
 /* Workspace bytes needed by either entry point for these sizes; 0 for invalid sizes. */
 size_t spec_verify_workspace_size(int32_t B, int32_t gamma, int64_t V, int dtype);
 

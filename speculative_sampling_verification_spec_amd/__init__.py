@@ -16,6 +16,7 @@ LIB_PATH = _PKG / "libspecverify.so"
 
 SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_MAX_GAMMA = 64
+SPEC_NGRAM_MAX_N = 64
 SPEC_OK = 0
 
 _lib = None
@@ -52,6 +53,8 @@ def lib():
                                          P]
         L.spec_verify_commit.restype = ctypes.c_int
         L.spec_verify_commit.argtypes = [P, P, P, i32, i32, P, i64, P, P, P, P]
+        L.spec_ngram_propose.restype = ctypes.c_int
+        L.spec_ngram_propose.argtypes = [P, i64, P, i32, i32, i32, i32, P, P, P, P, P]
         L.spec_verify_workspace_size.restype = sz
         L.spec_verify_workspace_size.argtypes = [i32, i32, i64, ctypes.c_int]
         L.spec_verify_strerror.restype = ctypes.c_char_p
@@ -204,6 +207,26 @@ def spec_verify_commit(out_tokens, out_num_accepted, gamma: int, seq_tokens, seq
         _dev(stats, "stats", torch.int64, 5),
         _dev(accept_hist, "accept_hist", torch.int64, int(gamma) + 1), _stream(stream))
     _check(rc, "spec_verify_commit")
+
+
+def spec_ngram_propose(seq_tokens, seq_len, n_min: int, n_max: int, gamma: int, out_counts,
+                       out_dense, out_cu=None, out_packed=None, stream=None) -> None:
+    """Prompt-lookup drafts for the contexts ``seq_tokens [B, capacity]`` (int32) of lengths
+    ``seq_len [B]``: ``out_counts [B]``, ``out_dense [B, gamma]`` and, optionally, the CSR pair
+    ``out_cu [B + 1]`` / ``out_packed [B * gamma]`` that spec_verify_* take as cu_draft /
+    draft_tokens.  ``B`` is ``seq_len.numel()``."""
+    torch = _torch()
+    B = seq_len.numel()
+    if seq_tokens.dim() != 2 or seq_tokens.shape[0] < B:
+        raise ValueError("seq_tokens must be [B, capacity]")
+    rc = lib().spec_ngram_propose(
+        _dev(seq_tokens, "seq_tokens", torch.int32), seq_tokens.shape[1],
+        _dev(seq_len, "seq_len", torch.int32, B), B, int(n_min), int(n_max), int(gamma),
+        _dev(out_counts, "out_counts", torch.int32, B),
+        _dev(out_dense, "out_dense", torch.int32, B * int(gamma)),
+        _dev(out_cu, "out_cu", torch.int32, B + 1),
+        _dev(out_packed, "out_packed", torch.int32, B * int(gamma)), _stream(stream))
+    _check(rc, "spec_ngram_propose")
 
 
 class PreparedCall:

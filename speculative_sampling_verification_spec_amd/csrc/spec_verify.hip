@@ -1104,6 +1104,116 @@ __global__ __launch_bounds__(kThreads) void k_commit(CommitParams C) {
       if (s_hist[i]) atomicAdd(&C.hist[i], (unsigned long long)s_hist[i]);
 }
 
+// ------------------------------------------------------------------ n-gram drafter
+
+constexpr int kNgramLoads = 16;  // context tokens per thread in flight
+
+struct NgramParams {
+  const int32_t *seq;
+  int64_t capacity;
+  const int32_t *seq_len;
+  int32_t B, n_min, n_max, gamma;
+  int32_t *counts, *dense, *cu, *packed;
+};
+
+// One workgroup per request.  With h the context and L its length, m(e) is the length of the
+// common run of h ending at e and h ending at L - 1 (compared backwards, capped at
+// n_hi = min(n_max, L - 1)), for every e < L - 1: an n-gram equal to the last n tokens ends
+// at e iff m(e) >= n.  So the longest usable n is the maximum of m, and its earliest
+// occurrence ends at the first e attaining it; one pass over the context and one block
+// reduction of the key (m, -e) give both.
+__global__ __launch_bounds__(kThreads) void k_ngram(NgramParams G) {
+  __shared__ int32_t s_suf[SPEC_NGRAM_MAX_N];  // s_suf[k] = h[L - 1 - k]
+  __shared__ unsigned long long s_key[kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t b = blockIdx.x;
+  const int32_t *h = G.seq + b * G.capacity;
+  int64_t L = G.seq_len[b];
+  L = L < 0 ? 0 : (L > G.capacity ? G.capacity : L);
+  const int32_t n_hi = (int32_t)(L - 1 < G.n_max ? L - 1 : G.n_max);
+  int32_t cnt = 0;
+  int64_t start = 0;
+  if (n_hi >= G.n_min) {  // uniform across the workgroup
+    if (tid < n_hi) s_suf[tid] = h[L - 1 - tid];
+    __syncthreads();
+    const int32_t last = s_suf[0];
+    // key = m << 32 | (2^31 - 1 - e): the maximum has the largest m and, for it, the
+    // smallest e.
+    unsigned long long key = 0;
+    for (int64_t e0 = 0; e0 < L - 1; e0 += (int64_t)kThreads * kNgramLoads) {
+      int32_t v[kNgramLoads];
+#pragma unroll
+      for (int q = 0; q < kNgramLoads; ++q) {
+        const int64_t e = e0 + q * kThreads + tid;
+        v[q] = e < L - 1 ? h[e] : 0;
+      }
+#pragma unroll
+      for (int q = 0; q < kNgramLoads; ++q) {
+        const int64_t e = e0 + q * kThreads + tid;
+        if (e < L - 1 && v[q] == last) {
+          int32_t k = 1;
+          while (k < n_hi && e - k >= 0 && h[e - k] == s_suf[k]) ++k;
+          const unsigned long long kk =
+              ((unsigned long long)k << 32) | (unsigned long long)(0x7fffffffll - e);
+          key = kk > key ? kk : key;
+        }
+      }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned long long t = __shfl_xor(key, o);
+      key = t > key ? t : key;
+    }
+    if (lane == 0) s_key[wave] = key;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) key = s_key[w] > key ? s_key[w] : key;
+    const int32_t n = (int32_t)(key >> 32);
+    if (n >= G.n_min) {
+      const int64_t e = 0x7fffffffll - (int64_t)(key & 0xffffffffull);
+      start = e + 1;  // the token after the occurrence (j + n with j = e - n + 1)
+      cnt = (int32_t)(L - start < G.gamma ? L - start : G.gamma);
+    }
+  }
+  for (int i = tid; i < G.gamma; i += kThreads)
+    G.dense[b * G.gamma + i] = i < cnt ? h[start + i] : -1;
+  if (tid == 0) G.counts[b] = cnt;
+}
+
+// One workgroup: running exclusive scan of the counts into cu (the verification step's CSR
+// over draft rows) and the proposals packed behind it, kNgramPackThreads requests at a time.
+constexpr int kNgramPackThreads = 1024;
+__global__ __launch_bounds__(kNgramPackThreads) void k_ngram_pack(NgramParams G) {
+  constexpr int NW = kNgramPackThreads / 64;
+  __shared__ int32_t s_tot[NW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int64_t base = 0;
+  for (int64_t b0 = 0; b0 < G.B; b0 += kNgramPackThreads) {
+    const int64_t b = b0 + tid;
+    const int32_t c = b < G.B ? G.counts[b] : 0;
+    int32_t inc = c;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t t = __shfl_up(inc, o);
+      if (lane >= o) inc += t;
+    }
+    if (lane == 63) s_tot[wave] = inc;
+    __syncthreads();
+    int32_t off = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (w < wave) off += s_tot[w];
+      total += s_tot[w];
+    }
+    __syncthreads();
+    const int64_t first = base + off + inc - c;
+    if (b < G.B) {
+      G.cu[b] = (int32_t)first;
+      for (int32_t i = 0; i < c; ++i) G.packed[first + i] = G.dense[b * G.gamma + i];
+    }
+    base += total;
+  }
+  if (tid == 0) G.cu[G.B] = (int32_t)base;
+}
+
 // ------------------------------------------------------------------ host side
 
 struct Plan {
@@ -1338,6 +1448,41 @@ int spec_verify_commit(const int32_t *out_tokens, const int32_t *out_num_accepte
   k_commit<<<dim3((uint32_t)ceil_div(B, kThreads)), dim3(kThreads), 0,
              static_cast<hipStream_t>(stream)>>>(C);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+int spec_ngram_propose(const int32_t *seq_tokens, int64_t capacity, const int32_t *seq_len,
+                       int32_t B, int32_t n_min, int32_t n_max, int32_t gamma,
+                       int32_t *out_counts, int32_t *out_dense, int32_t *out_cu,
+                       int32_t *out_packed, void *stream) {
+  if (B < 0 || capacity < 0 || n_min < 1 || n_max < n_min || n_max > SPEC_NGRAM_MAX_N ||
+      gamma < 0 || gamma > SPEC_MAX_GAMMA || capacity > (int64_t)INT32_MAX ||
+      (int64_t)B * gamma > (int64_t)INT32_MAX)
+    return SPEC_ERR_SHAPE;
+  if (B == 0) return SPEC_OK;
+  // with gamma == 0 nothing is written to out_dense or out_packed: they may be NULL
+  if (!seq_tokens || !seq_len || !out_counts || (gamma > 0 && !out_dense) ||
+      (gamma > 0 && (!out_cu) != (!out_packed)))
+    return SPEC_ERR_NULL;
+  NgramParams G = {};
+  G.seq = seq_tokens;
+  G.capacity = capacity;
+  G.seq_len = seq_len;
+  G.B = B;
+  G.n_min = n_min;
+  G.n_max = n_max;
+  G.gamma = gamma;
+  G.counts = out_counts;
+  G.dense = out_dense;
+  G.cu = out_cu;
+  G.packed = out_packed;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  k_ngram<<<dim3((uint32_t)B), dim3(kThreads), 0, s>>>(G);
+  if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
+  if (out_cu) {
+    k_ngram_pack<<<dim3(1), dim3(kNgramPackThreads), 0, s>>>(G);
+    if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
+  }
+  return SPEC_OK;
 }
 
 }  // extern "C"

@@ -17,13 +17,13 @@ FAKE = P(4096)   # never dereferenced: every call below fails validation first
 
 def declared_functions():
     text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
-    return sorted(set(re.findall(r"\b(spec_verify_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(spec_\w+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert names == ["spec_verify_commit", "spec_verify_greedy", "spec_verify_sample",
-                     "spec_verify_strerror", "spec_verify_workspace_size"]
+    assert names == ["spec_ngram_propose", "spec_verify_commit", "spec_verify_greedy",
+                     "spec_verify_sample", "spec_verify_strerror", "spec_verify_workspace_size"]
     lib = sv.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -111,3 +111,33 @@ def test_commit_rejects_bad_arguments_before_launching(kw, code):
 
 def test_commit_with_no_requests_is_a_no_op():
     assert _commit(B=0, out=None, n=None, seq=None, seq_len=None) == 0
+
+
+def _ngram(**kw):
+    a = dict(seq=FAKE, cap=32, ln=FAKE, B=2, n_min=1, n_max=3, gamma=4, counts=FAKE, dense=FAKE,
+             cu=None, packed=None, stream=None)
+    a.update(kw)
+    return sv.lib().spec_ngram_propose(a["seq"], a["cap"], a["ln"], a["B"], a["n_min"],
+                                       a["n_max"], a["gamma"], a["counts"], a["dense"], a["cu"],
+                                       a["packed"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), -2), (dict(n_min=0), -2), (dict(n_min=4, n_max=3), -2), (dict(n_max=65), -2),
+    (dict(gamma=65), -2), (dict(cap=-1), -2), (dict(cap=1 << 31), -2),
+    (dict(B=1 << 30, gamma=64), -2),
+    (dict(seq=None), -1), (dict(ln=None), -1), (dict(counts=None), -1), (dict(dense=None), -1),
+    (dict(cu=FAKE), -1), (dict(packed=FAKE), -1),
+])
+def test_ngram_rejects_bad_arguments_before_launching(kw, code):
+    assert _ngram(**kw) == code
+
+
+def test_ngram_outputs_may_be_null_when_nothing_is_proposed():
+    # gamma == 0: out_dense and out_packed are never written; the call proceeds to launch,
+    # so only the argument check is exercised here (B == 0 keeps it off the GPU)
+    assert _ngram(B=0, gamma=0, dense=None, cu=FAKE, packed=None) == 0
+
+
+def test_ngram_with_no_requests_is_a_no_op():
+    assert _ngram(B=0, seq=None, ln=None, counts=None, dense=None) == 0

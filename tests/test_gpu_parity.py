@@ -370,6 +370,97 @@ def test_commit_dense_layout_and_many_requests():
     np.testing.assert_array_equal(hi.cpu().numpy().view(np.uint64), hi_o)
 
 
+def _ngram_gpu(seq, length, n_min, n_max, gamma, packed=True):
+    import torch
+    import speculative_sampling_verification_spec_amd as sv
+    B = len(length)
+    d = dict(seq=torch.from_numpy(seq).cuda(), len=torch.from_numpy(length).cuda(),
+             counts=torch.full((B,), -7, dtype=torch.int32, device="cuda"),
+             dense=torch.full((B * gamma,), -7, dtype=torch.int32, device="cuda"),
+             cu=torch.full((B + 1,), -7, dtype=torch.int32, device="cuda") if packed else None,
+             packed=torch.full((max(B * gamma, 1),), -7, dtype=torch.int32, device="cuda")
+             if packed else None)
+    sv.spec_ngram_propose(d["seq"], d["len"], n_min, n_max, gamma, d["counts"], d["dense"],
+                          d["cu"], d["packed"])
+    torch.cuda.synchronize()
+    return d
+
+
+@pytest.mark.parametrize("alphabet,cap,n_min,n_max,gamma", [
+    (2, 300, 1, 1, 4), (3, 300, 2, 4, 8), (8, 1000, 1, 6, 5), (50, 5000, 3, 64, 64),
+    (32000, 9000, 2, 5, 8), (5, 100, 1, 3, 0),
+])
+def test_ngram_matches_oracle(alphabet, cap, n_min, n_max, gamma):
+    rng = np.random.default_rng(alphabet + cap)
+    B = 257
+    seq = rng.integers(0, alphabet, size=(B, cap)).astype(np.int32)
+    length = rng.integers(0, cap + 1, size=B).astype(np.int32)
+    length[:4] = [0, 1, 2, cap]
+    print(f"[gpu] ngram alphabet={alphabet} cap={cap} n={n_min}..{n_max} gamma={gamma}", flush=True)
+    o = oracle.ngram(seq, length, n_min, n_max, gamma)
+    d = _ngram_gpu(seq, length, n_min, n_max, gamma)
+    np.testing.assert_array_equal(d["counts"].cpu().numpy(), o["counts"])
+    np.testing.assert_array_equal(d["dense"].cpu().numpy().reshape(B, gamma), o["dense"])
+    np.testing.assert_array_equal(d["cu"].cpu().numpy(), o["cu"])
+    np.testing.assert_array_equal(d["packed"].cpu().numpy()[: o["cu"][-1]], o["packed"])
+    d2 = _ngram_gpu(seq, length, n_min, n_max, gamma, packed=False)
+    np.testing.assert_array_equal(d2["counts"].cpu().numpy(), o["counts"])
+
+
+def test_ngram_on_repetitive_contexts_many_requests():
+    seq, length = workloads.token_contexts(3000, 4096, seed=12)
+    o = oracle.ngram(seq, length, 2, 5, 8)
+    assert (o["counts"] > 0).mean() > 0.3
+    d = _ngram_gpu(seq, length, 2, 5, 8)
+    np.testing.assert_array_equal(d["counts"].cpu().numpy(), o["counts"])
+    np.testing.assert_array_equal(d["cu"].cpu().numpy(), o["cu"])
+    np.testing.assert_array_equal(d["packed"].cpu().numpy()[: o["cu"][-1]], o["packed"])
+
+
+def test_propose_verify_commit_chain_matches_oracle():
+    # n-gram proposals -> greedy verification -> commit, all on the device with no host
+    # round trip, against the same chain through the oracle.  The target rows are built from
+    # the oracle's proposals: argmax = the proposal up to a seeded break, then another token.
+    import torch
+    import speculative_sampling_verification_spec_amd as sv
+    B, cap, gamma, V = 400, 2048, 6, 4096
+    seq, length = workloads.token_contexts(B, cap, seed=5, alphabet=V, min_fill=0.4)
+    length = np.minimum(length, cap - gamma - 1).astype(np.int32)
+    o = oracle.ngram(seq, length, 2, 4, gamma)
+    counts = o["counts"]
+    rng = np.random.default_rng(9)
+    R_t = int(counts.sum()) + B
+    target = rng.normal(0.0, 1.0, size=(R_t, V))
+    t = 0
+    for b in range(B):
+        k = int(counts[b])
+        brk = int(rng.integers(0, k + 1))
+        for i in range(k + 1):
+            want = o["dense"][b, i] if i < k and i < brk else int(rng.integers(0, V))
+            target[t + i, want] += 10.0
+        t += k + 1
+    w = workloads.Workload("ngram-chain", "f32", B, gamma, V, workloads.encode(target, "f32"),
+                           np.zeros((max(int(counts.sum()), 1), V), dtype=np.float32),
+                           o["packed"].astype(np.int32), np.zeros((R_t, 2), dtype=np.float32),
+                           np.zeros(B, dtype=np.float32), o["cu"].astype(np.int32))
+    ov = oracle.verify(w, greedy=True)
+    seq_o, len_o = seq.copy(), length.copy()
+    oracle.commit(ov["out_tokens"], ov["num_accepted"], gamma, seq_o, len_o, cu_draft=w.cu_draft)
+    # device chain
+    d = _ngram_gpu(seq, length, 2, 4, gamma)
+    tgt = torch.from_numpy(w.target).cuda()
+    out = torch.full((R_t,), -7, dtype=torch.int32, device="cuda")
+    nacc = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    ws = sv.alloc_workspace(B, gamma, V, sv.SPEC_F32)
+    sv.spec_verify_greedy(tgt, d["packed"], gamma, out, nacc, ws, cu_draft=d["cu"])
+    sv.spec_verify_commit(out, nacc, gamma, d["seq"], d["len"], cu_draft=d["cu"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(nacc.cpu().numpy(), ov["num_accepted"])
+    np.testing.assert_array_equal(d["seq"].cpu().numpy(), seq_o)
+    np.testing.assert_array_equal(d["len"].cpu().numpy(), len_o)
+    assert 0 < ov["num_accepted"].sum() < counts.sum()
+
+
 # ----------------------------------------------------------------------- distribution
 
 def test_gpu_chi_square_emitted_tokens_follow_p():

@@ -323,3 +323,30 @@ def small(*, B: int, gamma: int, V: int, dtype: str = "f32", seed: int = 0,
                     gammas=gam, dense=not ragged, target_sigma=target_sigma,
                     draft_sigma=draft_sigma, temperatures=temperatures, seed=seed,
                     peaks=peaks, peak_rng_seed=seed + 6)
+
+
+# ----------------------------------------------------------------------------- token contexts
+
+def token_contexts(B: int, capacity: int, *, seed: int, alphabet: int = 32000,
+                   copy_frac: float = 0.5, min_fill: float = 0.5, span=(8, 64)):
+    """Seeded token histories that repeat themselves, as RAG answers and code edits do: each
+    context is a run of spans, each span either fresh tokens drawn from ``alphabet`` or (with
+    probability ``copy_frac``) a copy of an earlier stretch of the same context.  Returns
+    ``seq [B, capacity]`` int32 (zeros past each length) and ``lengths [B]`` int32, lengths
+    ~ U[min_fill * capacity, capacity]."""
+    rng = np.random.default_rng(seed)
+    seq = np.zeros((B, capacity), dtype=np.int32)
+    lengths = rng.integers(int(min_fill * capacity), capacity + 1, size=B).astype(np.int32)
+    for b in range(B):
+        L, pos = int(lengths[b]), 0
+        row = seq[b]
+        while pos < L:
+            n = min(int(rng.integers(span[0], span[1] + 1)), L - pos)
+            if pos >= span[0] and rng.random() < copy_frac:
+                src = int(rng.integers(0, pos - min(n, pos) + 1))
+                n = min(n, pos - src)
+                row[pos: pos + n] = row[src: src + n]
+            else:
+                row[pos: pos + n] = rng.integers(0, alphabet, size=n)
+            pos += n
+    return seq, lengths
