@@ -244,9 +244,44 @@ def main():
         "cpu_baseline": None,
     }
     result["commit"] = time_commit(sv, w, out, nacc, d=inputs[0], steps=args.steps)
+    result["ngram"] = time_ngram(sv, steps=args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+NGRAM = dict(B=512, capacity=8192, n_min=2, n_max=5, gamma=8, seed=77)
+
+
+def time_ngram(sv, steps):
+    """spec_ngram_propose (with the CSR packing) on self-repeating synthetic contexts: time
+    per call, and the context bytes it must read once over that time."""
+    import torch
+    import workloads
+    c = NGRAM
+    seq, length = workloads.token_contexts(c["B"], c["capacity"], seed=c["seed"])
+    B, g = c["B"], c["gamma"]
+    seq_d = torch.from_numpy(seq).cuda()
+    len_d = torch.from_numpy(length).cuda()
+    counts = torch.empty(B, dtype=torch.int32, device="cuda")
+    dense = torch.empty(B * g, dtype=torch.int32, device="cuda")
+    cu = torch.empty(B + 1, dtype=torch.int32, device="cuda")
+    packed = torch.empty(B * g, dtype=torch.int32, device="cuda")
+    call = lambda: sv.spec_ngram_propose(seq_d, len_d, c["n_min"], c["n_max"], g, counts,
+                                         dense, cu, packed)
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) * 1e6 / steps
+    nbytes = 4 * int(length.sum())
+    return {"workload": f"B={B} contexts of up to {c['capacity']} tokens (mean {length.mean():.0f}), "
+                        f"n {c['n_min']}..{c['n_max']}, gamma {g}",
+            "us_per_call": round(us, 2), "context_GB_per_s": round(nbytes / us / 1e3, 1),
+            "proposals_per_request": round(float(counts.float().mean()), 3)}
 
 
 def time_commit(sv, w, out, nacc, d, steps):
