@@ -95,6 +95,15 @@ def test_sliced_finish(B, gamma, V, dtype):
     _both(w, greedy=True)
 
 
+def test_single_draft_decode_batch():
+    # one draft per request (the single-token MTP case of the Perplexity page, "Planification
+    # MTP pour un jeton unique"): 2 target rows + 1 draft row per request, full vocabulary
+    temps = np.where(np.arange(256) % 5 == 0, 0.0, np.linspace(0.5, 1.1, 256))
+    w = workloads.small(B=256, gamma=1, V=128256, dtype="bf16", seed=61, temperatures=temps,
+                        target_sigma=3.0, draft_sigma=1.0)
+    _both(w)
+
+
 # ----------------------------------------------------------------------- edge cases
 
 def test_p_equal_q_accepts_everything_on_gpu():
