@@ -584,3 +584,80 @@ def test_ngram_proposals_continue_the_matched_window():
         assert c == min(gamma, 170 - (j + n)) and c >= 1
         np.testing.assert_array_equal(base[b, j: j + n], base[b, 170 - n: 170])
         np.testing.assert_array_equal(r["dense"][b, :c], base[b, j + n: j + n + c])
+
+
+# --------------------------------------------------------------------------- exact enumeration
+
+def _intervals(edges):
+    """Sub-intervals of [0, 1) cut at ``edges``: (midpoint, length) pairs."""
+    e = np.unique(np.clip(np.concatenate([[0.0], np.asarray(edges, dtype=np.float64), [1.0]]), 0, 1))
+    return [((a + b) / 2, b - a) for a, b in zip(e[:-1], e[1:]) if b - a > 1e-6]
+
+
+@pytest.mark.parametrize("V,seed", [(3, 1), (4, 2), (4, 3)])
+def test_exact_composition_by_enumeration(V, seed):
+    # gamma = 2.  Every draft pair (x0, x1), weighted q0(x0) q1(x1), and every interval of the
+    # three uniforms that matter (accept at 0, accept at 1, the stop row's draw) cut at the
+    # analytic thresholds min(1, p/q) and the CDF steps of the distribution drawn from.  The
+    # oracle is run once at each interval's midpoint and weighted by its length: this is the
+    # exact distribution of its output.  It must emit p0 at position 0, given n >= 1 p1 at
+    # position 1, and given n = 2 p2 at position 2 (to 1e-12), with
+    # P(n >= k) = prod_{i<k} sum_x min(p_i, q_i).
+    rng = np.random.default_rng(seed)
+    zt = rng.normal(0, 1.0, size=(3, V))
+    zd = rng.normal(0, 1.0, size=(2, V))
+    tr = workloads.decode(workloads.encode(zt, "f32"), "f32")
+    dr = workloads.decode(workloads.encode(zd, "f32"), "f32")
+    p = [_softmax(tr[i], 1.0) for i in range(3)]
+    q = [_softmax(dr[i], 1.0) for i in range(2)]
+
+    def cdf_edges(w):
+        c = np.cumsum(w)
+        return c / c[-1]
+
+    cases = []   # (weight, x0, x1, u rows)
+    for x0 in range(V):
+        for x1 in range(V):
+            wx = q[0][x0] * q[1][x1]
+            r0 = p[0][x0] / q[0][x0]
+            for ua0, la0 in _intervals([r0]):
+                if ua0 >= r0:   # rejected at 0: draw from (p0 - q0)+
+                    for us0, ls0 in _intervals(cdf_edges(np.maximum(p[0] - q[0], 0))):
+                        cases.append((wx * la0 * ls0, x0, x1, [[ua0, us0], [0.5, 0.5], [0.5, 0.5]]))
+                    continue
+                r1 = p[1][x1] / q[1][x1]
+                for ua1, la1 in _intervals([r1]):
+                    if ua1 >= r1:
+                        edges = cdf_edges(np.maximum(p[1] - q[1], 0))
+                        for us1, ls1 in _intervals(edges):
+                            cases.append((wx * la0 * la1 * ls1, x0, x1,
+                                          [[ua0, 0.5], [ua1, us1], [0.5, 0.5]]))
+                    else:
+                        for us2, ls2 in _intervals(cdf_edges(p[2])):
+                            cases.append((wx * la0 * la1 * ls2, x0, x1,
+                                          [[ua0, 0.5], [ua1, 0.5], [0.5, us2]]))
+    n = len(cases)
+    wts = np.array([c[0] for c in cases])
+    assert abs(wts.sum() - 1.0) < 1e-12
+    w = Workload("enum", "f32", n, 2, V, np.tile(workloads.encode(zt, "f32"), (n, 1)),
+                 np.tile(workloads.encode(zd, "f32"), (n, 1)),
+                 np.array([[c[1], c[2]] for c in cases], np.int32).ravel(),
+                 np.array([c[3] for c in cases], np.float32).reshape(3 * n, 2),
+                 np.ones(n, np.float32))
+    r = oracle.verify(w)
+    toks = r["out_tokens"].reshape(n, 3)
+    nacc = r["num_accepted"]
+    first = np.bincount(toks[:, 0], weights=wts, minlength=V)
+    np.testing.assert_allclose(first, p[0], rtol=0, atol=1e-12)
+    reach1 = nacc >= 1
+    beta = [np.minimum(p[i], q[i]).sum() for i in range(2)]
+    assert abs(wts[reach1].sum() - beta[0]) < 1e-12
+    assert abs(wts[nacc >= 2].sum() - beta[0] * beta[1]) < 1e-12
+    second = np.bincount(toks[reach1, 1], weights=wts[reach1], minlength=V) / wts[reach1].sum()
+    np.testing.assert_allclose(second, p[1], rtol=0, atol=1e-12)
+    reach2 = nacc >= 2   # every draft accepted: the bonus token comes from p2
+    third = np.bincount(toks[reach2, 2], weights=wts[reach2], minlength=V) / wts[reach2].sum()
+    np.testing.assert_allclose(third, p[2], rtol=0, atol=1e-12)
+    # accepted prefixes are the drafts themselves
+    d = w.draft_tokens.reshape(n, 2)
+    assert (toks[reach1, 0] == d[reach1, 0]).all()
