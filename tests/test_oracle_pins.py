@@ -661,3 +661,33 @@ def test_exact_composition_by_enumeration(V, seed):
     # accepted prefixes are the drafts themselves
     d = w.draft_tokens.reshape(n, 2)
     assert (toks[reach1, 0] == d[reach1, 0]).all()
+
+
+@pytest.mark.parametrize("T", [0.3, 1.0, 2.5])
+def test_inverse_cdf_matches_searchsorted(T):
+    # p = q accepts every draft, so the token at row gamma is the inverse CDF of p there with
+    # the row's draw uniform: numpy's searchsorted(cumsum(w), u * sum(w), 'right') is the first
+    # index whose running sum exceeds u R, in index order, skipping zero weights.
+    rng = np.random.default_rng(int(T * 10))
+    B, gamma, V = 3000, 1, 97
+    z = rng.normal(0, 2.0, size=(B * (gamma + 1), V))
+    z[:, ::7] = -1e4          # zero-weight tokens in exp: never drawn
+    T32 = float(np.float32(T))
+    tgt = workloads.encode(z, "f32")
+    dft = tgt.reshape(B, gamma + 1, V)[:, :gamma].reshape(B * gamma, V).copy()
+    tok = rng.integers(0, V, size=B * gamma).astype(np.int32)
+    tok[tok % 7 == 0] += 1
+    uni = rng.random((B * (gamma + 1), 2), dtype=np.float32)
+    w = Workload("icdf", "f32", B, gamma, V, tgt, dft, tok, uni, np.full(B, T32, np.float32))
+    r = oracle.verify(w)
+    assert (r["num_accepted"] == gamma).all()
+    zs = workloads.decode(tgt, "f32").reshape(B, gamma + 1, V)[:, gamma]
+    wts = np.exp((zs - zs.max(axis=1, keepdims=True)) / T32)
+    C = np.cumsum(wts, axis=1)
+    u = uni.reshape(B, gamma + 1, 2)[:, gamma, 1].astype(np.float64)
+    expect = np.array([np.searchsorted(C[b], u[b] * C[b, -1], side="right") for b in range(B)])
+    got = r["out_tokens"].reshape(B, gamma + 1)[:, gamma]
+    clear = r["cdf_gap"] > 1e-12          # ties within rounding of a CDF step: either is valid
+    assert clear.mean() > 0.99
+    np.testing.assert_array_equal(got[clear], expect[clear])
+    assert not np.isin(got, np.arange(0, V, 7)).any()
