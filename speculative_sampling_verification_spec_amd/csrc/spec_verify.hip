@@ -5,7 +5,7 @@
 // and emit a draw from max(p_j - q_j, 0) there, or from p_gamma when nothing was rejected;
 // at temperature zero, compare each draft with the target argmax instead.
 //
-// Two launches on the caller's stream, neither of which waits for the host:
+// A verification call is two launches on the caller's stream, neither waiting for the host:
 //
 //  k_rowstats  The HBM-bound stream.  Every needed logit row is read exactly once, cut into
 //              16K-element tiles, one workgroup per (row slot, slice) on a 2-D grid; slots a
@@ -14,21 +14,25 @@
 //              16-bit integer compares for bf16, wave shuffles, one LDS exchange), then sums
 //              2^((z - M) c), c = log2(e)/T: fp32 terms in a fixed pairwise tree over each
 //              thread's 64 elements, fp64 beyond.  Greedy rows (T = 0) reduce to (max, lowest
-//              argmax).  Output: one partial per (row, slice), and the row's logit at its
-//              draft token from the tile that holds it.
+//              argmax).  Output: one partial per (row, slice), and per row slot a record of
+//              the row's logit at its draft token, the token and its accept uniform.
 //
-//  k_finish    Workgroups (request, slice of the vocabulary).  Each one (1) merges its
-//              request's row partials (one wavefront per row, one lane per slice, fp64) and
-//              (2) runs the accept tests lane-parallel (p(x), q(x) in fp64 from the captured
-//              logits) with the first rejection from ballot + find-first-set; slice 0 writes
-//              the outputs.  For a sampled request every slice then (3) streams its part of the
-//              stop row(s) into one fp64 sum of S_t (p_k - q_k)_+ (or S_t p_k for the bonus) per
-//              64-unit chunk, and the last slice to finish (4) draws: a block scan over the
-//              request's chunk sums picks the chunk holding u * R, a wavefront scan over its 64
-//              units picks the unit, and a walk over the unit's elements gives the token.  The
-//              chunk sums cross workgroups as device-scope atomic stores and loads, ordered by
-//              a per-request arrival counter (which k_rowstats clears), so no cache writeback
-//              is needed inside the kernel.
+//  k_finish    Workgroups (slice of the vocabulary, request).  Each one (1) merges its
+//              request's row partials (a group of lanes per row slot, one lane per tile,
+//              fp64) and (2) runs the accept tests lane-parallel (p(x), q(x) in fp64 from the
+//              captured logits) with the first rejection from ballot + find-first-set; slice 0
+//              writes the outputs.  For a sampled request every slice then (3) streams its part
+//              of the stop row(s) into one fp64 sum of S_t (p_k - q_k)_+ (or S_t p_k for the
+//              bonus) per 64-unit chunk, and the last slice to finish (4) draws: a block scan
+//              over the request's chunk sums picks the chunk holding u * R, a wavefront scan
+//              over its 64 units picks the unit, and a walk over the unit's elements gives the
+//              token.  The chunk sums cross workgroups as device-scope atomic stores and loads,
+//              ordered by a per-request arrival counter (which k_rowstats clears), so no cache
+//              writeback is needed inside the kernel.
+//
+// After a call, for a serving loop that stays on the device: k_commit appends each
+// request's emitted tokens to its history and counts the step; k_ngram (+ k_ngram_pack)
+// drafts the next step by prompt lookup.
 //
 // Numerics: logits convert exactly to fp32; exponent arguments carry the temperature as a
 // two-float constant, so rounding never shifts the temperature, and their shifts are kept
