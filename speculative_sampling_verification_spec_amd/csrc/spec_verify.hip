@@ -1125,9 +1125,14 @@ struct NgramParams {
 // n_hi = min(n_max, L - 1)), for every e < L - 1: an n-gram equal to the last n tokens ends
 // at e iff m(e) >= n.  So the longest usable n is the maximum of m, and its earliest
 // occurrence ends at the first e attaining it; one pass over the context and one block
-// reduction of the key (m, -e) give both.
+// reduction of the key (m, -e) give both.  The context goes through LDS a round of
+// kNgramRound tokens at a time, behind a halo of the previous round's last SPEC_NGRAM_MAX_N
+// tokens, so the backward comparisons read LDS; the first round's loads go out with the
+// pattern's, and each next round's while the current one is compared.
+constexpr int kNgramRound = kThreads * kNgramLoads;
 __global__ __launch_bounds__(kThreads) void k_ngram(NgramParams G) {
   __shared__ int32_t s_suf[SPEC_NGRAM_MAX_N];  // s_suf[k] = h[L - 1 - k]
+  __shared__ int32_t s_ctx[SPEC_NGRAM_MAX_N + kNgramRound];  // halo, then the round
   __shared__ unsigned long long s_key[kWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t b = blockIdx.x;
@@ -1138,29 +1143,51 @@ __global__ __launch_bounds__(kThreads) void k_ngram(NgramParams G) {
   int32_t cnt = 0;
   int64_t start = 0;
   if (n_hi >= G.n_min) {  // uniform across the workgroup
+    const int64_t E = L - 1;  // candidate ends e < E
+    int32_t v[kNgramLoads];
+#pragma unroll
+    for (int q = 0; q < kNgramLoads; ++q) {
+      const int64_t e = q * kThreads + tid;
+      v[q] = e < E ? h[e] : 0;
+    }
     if (tid < n_hi) s_suf[tid] = h[L - 1 - tid];
-    __syncthreads();
-    const int32_t last = s_suf[0];
     // key = m << 32 | (2^31 - 1 - e): the maximum has the largest m and, for it, the
     // smallest e.
     unsigned long long key = 0;
-    for (int64_t e0 = 0; e0 < L - 1; e0 += (int64_t)kThreads * kNgramLoads) {
-      int32_t v[kNgramLoads];
+    for (int64_t e0 = 0; e0 < E; e0 += kNgramRound) {
 #pragma unroll
-      for (int q = 0; q < kNgramLoads; ++q) {
-        const int64_t e = e0 + q * kThreads + tid;
-        v[q] = e < L - 1 ? h[e] : 0;
+      for (int q = 0; q < kNgramLoads; ++q) s_ctx[SPEC_NGRAM_MAX_N + q * kThreads + tid] = v[q];
+      __syncthreads();
+      const int32_t last = s_suf[0];
+      int32_t cur[kNgramLoads];
+#pragma unroll
+      for (int q = 0; q < kNgramLoads; ++q) cur[q] = v[q];
+      const int64_t e1 = e0 + kNgramRound;
+      if (e1 < E) {  // the next round's loads go out before this round is compared
+#pragma unroll
+        for (int q = 0; q < kNgramLoads; ++q) {
+          const int64_t e = e1 + q * kThreads + tid;
+          v[q] = e < E ? h[e] : 0;
+        }
       }
 #pragma unroll
       for (int q = 0; q < kNgramLoads; ++q) {
         const int64_t e = e0 + q * kThreads + tid;
-        if (e < L - 1 && v[q] == last) {
+        if (e < E && cur[q] == last) {
+          const int32_t at = SPEC_NGRAM_MAX_N + q * kThreads + tid;  // e's slot in s_ctx
           int32_t k = 1;
-          while (k < n_hi && e - k >= 0 && h[e - k] == s_suf[k]) ++k;
+          while (k < n_hi && e - k >= 0 && s_ctx[at - k] == s_suf[k]) ++k;
           const unsigned long long kk =
               ((unsigned long long)k << 32) | (unsigned long long)(0x7fffffffll - e);
           key = kk > key ? kk : key;
         }
+      }
+      __syncthreads();  // every comparison of this round is done
+      if (e1 < E) {     // uniform: this round was full, its tail becomes the next halo
+        int32_t t = 0;
+        if (tid < SPEC_NGRAM_MAX_N) t = s_ctx[kNgramRound + tid];
+        __syncthreads();  // the tail is read before the next round overwrites it
+        if (tid < SPEC_NGRAM_MAX_N) s_ctx[tid] = t;
       }
     }
     for (int o = 32; o > 0; o >>= 1) {

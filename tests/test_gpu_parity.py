@@ -394,6 +394,7 @@ def _ngram_gpu(seq, length, n_min, n_max, gamma, packed=True):
 @pytest.mark.parametrize("alphabet,cap,n_min,n_max,gamma", [
     (2, 300, 1, 1, 4), (3, 300, 2, 4, 8), (8, 1000, 1, 6, 5), (50, 5000, 3, 64, 64),
     (32000, 9000, 2, 5, 8), (5, 100, 1, 3, 0),
+    (2, 12000, 1, 64, 8),      # long matches across rounds of the LDS-staged context
 ])
 def test_ngram_matches_oracle(alphabet, cap, n_min, n_max, gamma):
     rng = np.random.default_rng(alphabet + cap)
