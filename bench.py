@@ -29,8 +29,10 @@ sys.path.insert(0, str(ROOT))
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MALL_BYTES = 256 << 20          # last-level (Infinity) cache
-# launches of one call: row statistics, then accept tests + residual + draw
-KERNELS = ["k_rowstats", "k_finish"]
+# launches of one call: row statistics, then accept tests + residual + draw (two-launch
+# path), or the whole step (one-launch path, small calls)
+KERNELS = {"two": ["k_rowstats", "k_finish"], "one": ["k_onepass"]}
+PATHS = {"auto": 0, "two": 1, "one": 2}
 DEFAULT_WORKLOAD = 5
 WARMUP_SECONDS = 0.25
 PROFILES = ROOT / "profiles"
@@ -70,10 +72,10 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def traffic_for_current_kernel(workload: int):
-    """HBM bytes per k_rowstats launch from the committed rocprofv3 counter runs for this
+def traffic_for_current_kernel(kernel: str, workload: int):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter runs for this
     workload, or None if there are none or the kernel source changed since they were taken."""
-    path = PROFILES / f"k_rowstats_workload{workload}_traffic.json"
+    path = PROFILES / f"{kernel}_workload{workload}_traffic.json"
     if not path.exists():
         return None
     rec = json.loads(path.read_text())
@@ -132,6 +134,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the plain copy the byte counters are calibrated with")
+    ap.add_argument("--path", choices=sorted(PATHS), default="auto",
+                    help="launch path: the library's choice (auto), two launches, or one")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -164,8 +168,10 @@ def main():
     out = torch.empty(w.R_t, dtype=torch.int32, device="cuda")
     nacc = torch.empty(w.B, dtype=torch.int32, device="cuda")
     hip = HipEvents()
+    path = PATHS[args.path]
 
     def step(k, probe):
+        probe = probe if probe is not None or path == 0 else sv.make_probe(path=path)
         d = inputs[k % copies]
         sv.spec_verify_sample(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temps"],
                               w.gamma, out, nacc, ws, cu_draft=d["cu"], probe=probe)
@@ -184,8 +190,10 @@ def main():
     # Timed region A: the step time, with nothing on the stream but the library's kernels
     # (on this stack every recorded event leaves the GPU idle for several microseconds), and
     # each input copy's call marshalled once, as a serving loop would hold it.
+    ctl = sv.make_probe(path=path) if path else None
     calls = [sv.prepare_sample(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temps"],
-                               w.gamma, out, nacc, ws, cu_draft=d["cu"]) for d in inputs]
+                               w.gamma, out, nacc, ws, cu_draft=d["cu"], probe=ctl)
+             for d in inputs]
     t0 = time.perf_counter()
     for k in range(args.steps):
         calls[k % copies]()
@@ -193,24 +201,40 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
+    # Which launch path the calls took: the second launch's events are recorded only by
+    # the two-launch path.
+    evs = hip.create(4)
+    step(0, sv.make_probe(events=evs, path=path))
+    torch.cuda.synchronize()
+    try:
+        hip.elapsed_ms(evs[2], evs[3])
+        taken = "two"
+    except RuntimeError:
+        hip.hip.hipGetLastError()
+        taken = "one"
+    hip.destroy(evs)
+    kernels = KERNELS[taken]
+
     # Timed region B: the same steps again with per-kernel durations from events that each
     # kernel's dispatch records (probe events) on the stream it runs on.
-    n_ev = 2 * len(KERNELS)
+    n_ev = 2 * len(kernels)
     evs = hip.create(n_ev * args.steps)
-    probes = [sv.make_probe(events=evs[n_ev * k: n_ev * (k + 1)]) for k in range(args.steps)]
+    probes = [sv.make_probe(events=evs[n_ev * k: n_ev * (k + 1)], path=path)
+              for k in range(args.steps)]
     for k in range(args.steps):
         step(k, probes[k])
     torch.cuda.synchronize()
     per_kernel = {name: np.array([1e3 * hip.elapsed_ms(evs[n_ev * k + 2 * i], evs[n_ev * k + 2 * i + 1])
                                   for k in range(args.steps)])
-                  for i, name in enumerate(KERNELS)}
+                  for i, name in enumerate(kernels)}
     hip.destroy(evs)
     per_kernel_us = {name: round(float(d.mean()), 2) for name, d in per_kernel.items()}
-    rs_all = per_kernel["k_rowstats"]
+    # the dominant kernel: the row-statistics stream, or the one launch that does everything
+    rs_all = per_kernel[kernels[0]]
     rs_us = float(rs_all.mean())
 
     achieved = nbytes / (rs_us * 1e-6) / 1e9
-    traffic = traffic_for_current_kernel(args.workload)
+    traffic = traffic_for_current_kernel(kernels[0], args.workload)
     positions = w.positions
     value = positions / (ms_per_step * 1e-3)
     logit_gbps = nbytes / (ms_per_step * 1e-3) / 1e9
@@ -230,11 +254,11 @@ def main():
         "config": {"workload": f"{args.workload}: {w.name}", "B": w.B, "gamma_max": w.gamma,
                    "V": w.V, "logit_dtype": w.dtype, "positions_per_step": positions,
                    "logit_bytes_per_step": nbytes, "input_copies": copies,
-                   "parallelism": "single GPU"},
+                   "launch_path": taken, "parallelism": "single GPU"},
         "logit_GB_per_s": round(logit_gbps, 1),
         "hbm_frac": round(logit_gbps / HBM_PEAK_GBPS, 4),
         "kernel_us": per_kernel_us,
-        "roofline": {"bound": "hbm", "kernel": "k_rowstats", "kernel_us": round(rs_us, 2),
+        "roofline": {"bound": "hbm", "kernel": kernels[0], "kernel_us": round(rs_us, 2),
                      "kernel_us_p10_p50_p90": [round(float(np.percentile(rs_all, q)), 1)
                                                for q in (10, 50, 90)],
                      "achieved": round(achieved, 1),

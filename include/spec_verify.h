@@ -63,8 +63,8 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
 enum {
   SPEC_OK = 0,
   SPEC_ERR_NULL = -1,       /* a required pointer is NULL                                */
-  SPEC_ERR_SHAPE = -2,      /* B < 0, gamma not in [0, 64], V not in [1, 2^24], or a
-                               grid too large                                            */
+  SPEC_ERR_SHAPE = -2,      /* B < 0, gamma not in [0, 64], V not in [1, 2^24], a grid
+                               too large, or a launch path the call cannot take          */
   SPEC_ERR_DTYPE = -3,      /* dtype is not a spec_dtype                                 */
   SPEC_ERR_WORKSPACE = -4,  /* workspace smaller than spec_verify_workspace_size, or not
                                256-byte aligned                                          */
@@ -75,8 +75,30 @@ enum {
 #define SPEC_MAX_GAMMA 64
 
 /*
- * Optional diagnostics.  Every pointer may be NULL; all are device pointers except
- * `events`.  Entries of greedy requests are written only where stated.
+ * How a verification call is launched (spec_probe.path).  Both ways compute the same step.
+ *  SPEC_PATH_TWO  two launches: a row-statistics stream over every needed logit, then one that
+ *                 merges, tests, sums the stop rows and draws.  Any size.
+ *  SPEC_PATH_ONE  one launch for small calls: each workgroup takes one column slice of every
+ *                 row of its request, and the few workgroups of a request meet inside the
+ *                 launch (device-scope atomics and bounded polling), so the call costs one
+ *                 kernel boundary instead of two.  Requires B <= 2048, V <= 262144 and all of
+ *                 the call's workgroups resident on the device at once (checked against the
+ *                 device's capacity for the kernel).  A request whose workgroups do not all
+ *                 arrive within a bounded wait (seconds; only if other work keeps them from
+ *                 being resident) comes back with out_num_accepted = -1.
+ *  SPEC_PATH_AUTO the library's choice, the default: two launches.  On MI355X the one-launch
+ *                 path measured slower at every size tried, small batches included: the
+ *                 handoff between workgroups inside the launch costs about as many dependent
+ *                 memory round trips as the kernel boundary it removes.
+ */
+#define SPEC_PATH_AUTO 0
+#define SPEC_PATH_TWO 1
+#define SPEC_PATH_ONE 2
+
+/*
+ * Optional diagnostics and launch control (NULL: none, SPEC_PATH_AUTO).  Every pointer may be
+ * NULL; all are device pointers except `events`.  Entries of greedy requests are written
+ * only where stated.
  */
 typedef struct spec_probe {
   double *p_x;        /* [R_d] p_i(x_i) at each draft position of sampled requests         */
@@ -89,9 +111,12 @@ typedef struct spec_probe {
                          stop row: sum_k max(p_k - q_k, 0) after a rejection, sum_k p_k
                          (= 1) for the bonus; sampled requests                            */
   void *events[8];    /* host: hipEvent_t or NULL; events[2k] / events[2k+1] are recorded by
-                         the dispatch of the call's k-th kernel as it starts / ends (launch 0:
-                         row statistics, launch 1: accept tests, residual and draw); the
-                         entries for k = 2, 3 are not touched                             */
+                         the dispatch of the call's k-th kernel as it starts / ends (two
+                         launches: 0 row statistics, 1 accept tests, residual and draw; one
+                         launch: 0 the whole step); entries of launches not made are not
+                         touched                                                        */
+  int path;           /* SPEC_PATH_AUTO, _TWO or _ONE; _ONE on a call that cannot take it,
+                         or another value, returns SPEC_ERR_SHAPE                         */
 } spec_probe;
 
 /*
@@ -111,7 +136,10 @@ typedef struct spec_probe {
  *                                  token emitted at the stop row n_b, then -1
  *  out_num_accepted [B] int32      n_b in [0, gamma_b]; the step emits n_b + 1 tokens
  *  workspace      device scratch of at least spec_verify_workspace_size(B, gamma, V, dtype)
- *                 bytes, 256-byte aligned; no initial contents are required
+ *                 bytes, 256-byte aligned, zero-filled before its first use; every call
+ *                 leaves it ready for the next, of any shape.  Its first 16 KiB hold the
+ *                 one-launch path's per-request counters, which each call returns to zero;
+ *                 the rest needs no initial contents
  *  probe          NULL, or diagnostics as above
  *  stream         hipStream_t
  *

@@ -18,6 +18,7 @@ SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_MAX_GAMMA = 64
 SPEC_NGRAM_MAX_N = 64
 SPEC_OK = 0
+SPEC_PATH_AUTO, SPEC_PATH_TWO, SPEC_PATH_ONE = 0, 1, 2
 
 _lib = None
 
@@ -32,7 +33,8 @@ class _Probe(ctypes.Structure):
     _fields_ = [("p_x", ctypes.c_void_p), ("q_x", ctypes.c_void_p),
                 ("row_max_t", ctypes.c_void_p), ("row_sum_t", ctypes.c_void_p),
                 ("row_max_d", ctypes.c_void_p), ("row_sum_d", ctypes.c_void_p),
-                ("resid_mass", ctypes.c_void_p), ("events", ctypes.c_void_p * 8)]
+                ("resid_mass", ctypes.c_void_p), ("events", ctypes.c_void_p * 8),
+                ("path", ctypes.c_int)]
 
 
 def lib():
@@ -109,9 +111,9 @@ def _stream(stream):
 
 
 def make_probe(p_x=None, q_x=None, row_max_t=None, row_sum_t=None, row_max_d=None,
-               row_sum_d=None, resid_mass=None, events=None) -> _Probe:
-    """Diagnostics struct; tensors (device) or None, ``events`` a list of up to 8 raw
-    hipEvent_t handles (ints) or None."""
+               row_sum_d=None, resid_mass=None, events=None, path=SPEC_PATH_AUTO) -> _Probe:
+    """Diagnostics and launch-control struct; tensors (device) or None, ``events`` a list of
+    up to 8 raw hipEvent_t handles (ints) or None, ``path`` one of SPEC_PATH_*."""
     pr = _Probe()
     torch = _torch()
     for name, t, dt in (("p_x", p_x, torch.float64), ("q_x", q_x, torch.float64),
@@ -124,6 +126,7 @@ def make_probe(p_x=None, q_x=None, row_max_t=None, row_sum_t=None, row_max_d=Non
         setattr(pr, name, p.value if p is not None else None)
     for i, e in enumerate(events or []):
         pr.events[i] = e
+    pr.path = int(path)
     return pr
 
 
@@ -260,10 +263,10 @@ def prepare_greedy(target_logits, draft_tokens, gamma: int, out_tokens, out_num_
 
 
 def alloc_workspace(B: int, gamma: int, V: int, dtype: int, device="cuda"):
-    """uint8 device tensor of the size the library asks for (torch's allocations are
-    256-byte aligned)."""
+    """Zero-filled uint8 device tensor of the size the library asks for (torch's allocations
+    are 256-byte aligned); calls leave it ready for the next call of any shape."""
     torch = _torch()
     n = spec_verify_workspace_size(B, gamma, V, dtype)
     if n == 0:
         raise ValueError("invalid sizes for spec_verify")
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)

@@ -30,6 +30,11 @@
 //              ordered by a per-request arrival counter (which k_rowstats clears), so no cache
 //              writeback is needed inside the kernel.
 //
+// k_onepass, on request only (the probe's path field): the whole step in one launch for
+// calls whose workgroups all fit on the device at once; workgroup (request, column slice) over
+// every row of its request, the request's workgroups meeting on an arrival counter.  It gives
+// the same results and measured slower here, so two launches stay the default.
+//
 // After a call, for a serving loop that stays on the device: k_commit appends each
 // request's emitted tokens to its history and counts the step; k_ngram (+ k_ngram_pack)
 // drafts the next step by prompt lookup.
@@ -62,6 +67,12 @@ constexpr int kFinRU = 4;                    // k_finish: units per thread per r
 constexpr int kFinPassUnits = kThreads * kFinRU;  // k_finish: stop-row units per pass
 constexpr int kFinGrid = 1024;               // k_finish workgroups aimed for
 constexpr int kChunkUnits = 64;              // residual sums: one per 64 units (a wavefront load)
+constexpr int64_t kOneTileBytes = 16384;     // one-launch path: bytes per row per workgroup
+constexpr int64_t kOneAlign = 512;           // one-launch slices: whole chunks for every unit width
+constexpr int kOneMaxSlices = 32;            // one-launch workgroups per request, at most
+constexpr int kOneTargetWgs = 256;           // one-launch grid aimed for when rows are few
+constexpr int kOneMaxB = 2048;               // requests the one-launch counters cover
+constexpr uint32_t kSpinLimit = 1u << 22;    // polls before a one-launch workgroup stops waiting
 constexpr int64_t kMaxV = int64_t(1) << 24;
 constexpr double kLog2e = 1.4426950408889634074;
 constexpr size_t kAlign = 256;
@@ -113,6 +124,7 @@ struct Params {
   double *chunk_sums;       // [B][chunk_stride] residual sums per 64-unit chunk
   int64_t chunk_stride;
   uint32_t *done;           // [B] k_finish slices of each request finished (k_rowstats clears)
+  uint32_t *arrive, *odone; // [kOneMaxB] one-launch counters: zero before and after every call
   int32_t nslice;           // k_finish workgroups per request
   int64_t slice_units;      // stop-row units per k_finish workgroup (a multiple of 64)
   int32_t spr;              // row slots per request: 2*gamma+1 (sample) or gamma+1 (greedy)
@@ -425,13 +437,192 @@ __device__ int32_t block_last(bool pred, int32_t *sh) {
   return r;
 }
 
-// ------------------------------------------------------------------ k_rowstats
+// ------------------------------------------------------------------ row statistics of a tile
 
 struct StatsLds {
   float mx[kRsWaves];
   double sum[kRsWaves];
   int32_t idx[kRsWaves];
 };
+
+// Values a workgroup hands to another workgroup of the same launch (the one-launch path) are
+// written and read with device-scope atomics (SHARED); between two launches plain accesses
+// suffice, the kernel boundary orders them.
+template <bool SHARED>
+__device__ __forceinline__ void put_partial(Partial *p, const Partial &v) {
+  if constexpr (SHARED) {
+    const unsigned long long lo = (unsigned long long)__float_as_uint(v.m) |
+                                  ((unsigned long long)(uint32_t)v.idx << 32);
+    __hip_atomic_store(reinterpret_cast<unsigned long long *>(p), lo, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    share_store(&p->s, v.s);
+  } else {
+    *p = v;
+  }
+}
+template <bool SHARED>
+__device__ __forceinline__ Partial get_partial(const Partial *p) {
+  if constexpr (SHARED) {
+    const unsigned long long lo =
+        __hip_atomic_load(reinterpret_cast<unsigned long long *>(const_cast<Partial *>(p)),
+                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    Partial v;
+    v.m = __uint_as_float((uint32_t)lo);
+    v.idx = (int32_t)(uint32_t)(lo >> 32);
+    v.s = share_load(&p->s);
+    return v;
+  } else {
+    return *p;
+  }
+}
+template <bool SHARED>
+__device__ __forceinline__ void put_u32(void *p, uint32_t v) {
+  if constexpr (SHARED)
+    __hip_atomic_store(static_cast<uint32_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *static_cast<uint32_t *>(p) = v;
+}
+template <bool SHARED>
+__device__ __forceinline__ SlotRec get_rec(const SlotRec *p) {
+  if constexpr (SHARED) {
+    unsigned long long *q = reinterpret_cast<unsigned long long *>(const_cast<SlotRec *>(p));
+    const unsigned long long a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long c =
+        __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    SlotRec r;
+    r.z = __uint_as_float((uint32_t)a);
+    r.tok = (int32_t)(uint32_t)(a >> 32);
+    r.u = __uint_as_float((uint32_t)c);
+    r.pad = 0;
+    return r;
+  } else {
+    return *p;
+  }
+}
+
+// A row tile's nu units, NV per thread (unit j * kRsThreads + tid), with 16-byte nontemporal
+// loads issued together; units past nu hold the filler.
+template <int DT, bool VEC, int NV>
+__device__ __forceinline__ void load_tile(const typename Unit<DT, VEC>::Store *tile, int32_t nu,
+                                          typename Unit<DT, VEC>::Raw (&raw)[NV]) {
+  using U = Unit<DT, VEC>;
+  const int tid = threadIdx.x;
+  if (nu == kRsThreads * NV) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) raw[j] = U::template load<true>(tile, j * kRsThreads + tid);
+  } else {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int32_t u = j * kRsThreads + tid;
+      raw[j] = u < nu ? U::template load<true>(tile, u) : U::filler();
+    }
+  }
+}
+
+// Statistics of the row tile [lo, hi) (nu units, in registers from load_tile) by a workgroup of
+// kRsThreads: the tile maximum M, then for a sampled row (T > 0) the sum of 2^((z - M) c) and
+// for a greedy row the lowest index holding M, written to `out`.  The logit at `tok`, if the
+// tile holds it, goes to `zrec`.  Called by every thread of the workgroup.
+template <int DT, bool VEC, int NV, bool SHARED>
+__device__ __forceinline__ void tile_stats(const typename Unit<DT, VEC>::Raw (&raw)[NV],
+                                           const typename Unit<DT, VEC>::Store *tile,
+                                           int32_t nu, int64_t lo, int64_t hi, float T,
+                                           int32_t tok, Partial *out, float *zrec,
+                                           StatsLds &sh) {
+  using U = Unit<DT, VEC>;
+  constexpr int W = U::W;
+  constexpr int NT = kRsThreads;
+  constexpr int NW = kRsWaves;
+  const int tid = threadIdx.x;
+  const float tm = U::thread_max(raw);
+  const float M = block_max1<NW>(tm, sh.mx);
+
+  // The logit at the row's draft token, for the accept tests: written by the thread holding
+  // it, in the one tile that does.
+  if (tok >= lo && tok < hi) {
+    const int32_t off = (int32_t)(tok - lo);
+    const int32_t uo = off / W;
+    if (uo % NT == tid) {
+      float z = 0.f;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        if (j == uo / NT) {
+          float xv[W];
+          U::cvt(raw[j], xv);
+#pragma unroll
+          for (int q = 0; q < W; ++q)
+            if (q == off % W) z = xv[q];
+        }
+      }
+      put_u32<SHARED>(zrec, __float_as_uint(z));
+    }
+  }
+
+  if (T > 0.f) {
+    const TempConst tc = temp_const(T);
+    if (fold_ok(M, tc.c_hi) && tc.c < 1e6 && tc.c > 1e-30) {
+      // The common case: two-FMA exponent arguments.  In this range of c a filler's
+      // argument is -inf or below -200, so its term is exactly 0 and needs no mask.
+      const float K = (float)((double)M * tc.c);
+      // Unit sums, then a fixed pairwise tree over the thread's NV units in fp32 (at most 64
+      // terms of at most ~1.4 each: at most ~6 roundings, 3.6e-7 relative); everything
+      // beyond the thread is fp64.
+      float us[NV];
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        float x[W], e[W];
+        U::cvt(raw[j], x);
+#pragma unroll
+        for (int q = 0; q < W; ++q) e[q] = ex2(arg_folded(x[q], K, tc.c_hi, tc.c_lo));
+        us[j] = unit_sum<W>(e);
+      }
+#pragma unroll
+      for (int st = 1; st < NV; st *= 2) {
+#pragma unroll
+        for (int j = 0; j + st < NV; j += 2 * st) us[j] += us[j + st];
+      }
+      const double S = block_sum1<NW>((double)us[0], sh.sum);
+      // to the shifted form, sum 2^((z - M) c): factor 2^(K - M c), one rounding
+      if (tid == 0) put_partial<SHARED>(out, Partial{M, 0, S * exp2(fma(-(double)M, tc.c, (double)K))});
+    } else {
+      // Extreme temperatures or logits: overflow-safe arguments, units re-read one at a time
+      // (cache hits) to keep this rare path out of the common path's registers.
+      double acc = 0.0;
+#pragma unroll 1
+      for (int j = 0; j < NV; ++j) {
+        const int32_t u = j * NT + tid;
+        if (u < nu) {
+          float x[W], e[W];
+          U::cvt(U::template load<false>(tile, u), x);
+#pragma unroll
+          for (int q = 0; q < W; ++q) e[q] = ex2(arg_shifted(x[q], M, tc.c_hi, tc.c_lo));
+          acc += (double)unit_sum<W>(e);
+        }
+      }
+      const double S = block_sum1<NW>(acc, sh.sum);
+      if (tid == 0) put_partial<SHARED>(out, Partial{M, 0, S});
+    }
+  } else {
+    // Greedy row: the lowest index holding the tile maximum; only threads whose own maximum
+    // equals it search their units.
+    int32_t ti = INT32_MAX;
+    if (tm == M) {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        float x[W];
+        U::cvt(raw[j], x);
+        const int32_t u = j * NT + tid;
+#pragma unroll
+        for (int q = 0; q < W; ++q)
+          if (ti == INT32_MAX && u < nu && x[q] == M) ti = (int32_t)((lo / W + u) * W + q);
+      }
+    }
+    const int32_t bi = block_min1<NW>(ti, sh.idx);
+    if (tid == 0) put_partial<SHARED>(out, Partial{M, bi, 0.0});
+  }
+}
+
+// ------------------------------------------------------------------ k_rowstats
 
 // One workgroup per (row slot, tile): blockIdx.x is the tile of the row, blockIdx.y +
 // blockIdx.z * gridDim.y the row slot (request * spr + slot).  Slots beyond a request's rows
@@ -441,9 +632,7 @@ __global__ __launch_bounds__(kRsThreads) void k_rowstats(Params P) {
   using U = Unit<DT, VEC>;
   using Store = typename U::Store;
   constexpr int W = U::W;
-  constexpr int NT = kRsThreads;
-  constexpr int NW = kRsWaves;
-  constexpr int NV = int(kTileElems / NT) / W;  // units per thread
+  constexpr int NV = int(kTileElems / kRsThreads) / W;  // units per thread
   __shared__ StatsLds sh;
   const int tid = threadIdx.x;
   const uint32_t slot = blockIdx.y + blockIdx.z * gridDim.y;
@@ -471,7 +660,6 @@ __global__ __launch_bounds__(kRsThreads) void k_rowstats(Params P) {
     pos = i;
   }
   const int32_t xtok = pos < gb ? P.tokens[dbase + pos] : -1;
-  const int32_t tok = T > 0.f ? xtok : -1;
   if (k <= P.gamma && pos < gb && blockIdx.x == 0 && tid == 0) {
     P.rec[slot].tok = xtok;
     P.rec[slot].u = T > 0.f ? P.uniforms[2 * (dbase + b + pos)] : 0.f;
@@ -483,106 +671,11 @@ __global__ __launch_bounds__(kRsThreads) void k_rowstats(Params P) {
   const int64_t hi = lo + P.split_len < P.V ? lo + P.split_len : P.V;
   const Store *tile = static_cast<const Store *>(row_ptr<DT>(base, row, P.V)) + lo / W;
   const int32_t nu = (int32_t)((hi - lo + W - 1) / W);
-
-  // The tile's loads go out before anything else; units past the row end hold the filler.
   typename U::Raw raw[NV];
-  if (nu == NT * NV) {
-#pragma unroll
-    for (int j = 0; j < NV; ++j) raw[j] = U::template load<true>(tile, j * NT + tid);
-  } else {
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int32_t u = j * NT + tid;
-      raw[j] = u < nu ? U::template load<true>(tile, u) : U::filler();
-    }
-  }
-  const float tm = U::thread_max(raw);
-  const float M = block_max1<NW>(tm, sh.mx);
-  Partial *out = P.parts + (int64_t)slot * P.nsplit + blockIdx.x;
-
-  // The logit at the row's draft token, for k_finish's accept tests: written by the thread
-  // holding it, in the one tile that does.
-  if (tok >= lo && tok < hi) {
-    const int32_t off = (int32_t)(tok - lo);
-    const int32_t uo = off / W;
-    if (uo % NT == tid) {
-      float z = 0.f;
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        if (j == uo / NT) {
-          float xv[W];
-          U::cvt(raw[j], xv);
-#pragma unroll
-          for (int q = 0; q < W; ++q)
-            if (q == off % W) z = xv[q];
-        }
-      }
-      P.rec[slot].z = z;
-    }
-  }
-
-  if (T > 0.f) {
-    const TempConst tc = temp_const(T);
-    if (fold_ok(M, tc.c_hi) && tc.c < 1e6 && tc.c > 1e-30) {
-      // The common case: two-FMA exponent arguments.  In this range of c a filler's
-      // argument is -inf or below -200, so its term is exactly 0 and needs no mask.
-      const float K = (float)((double)M * tc.c);
-      // Unit sums, then a fixed pairwise tree over the thread's NV units in fp32: 64 terms
-      // of at most ~1.4 each, so the thread's sum carries at most ~6 roundings (3.6e-7
-      // relative); everything beyond the thread is fp64.
-      float us[NV];
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        float x[W], e[W];
-        U::cvt(raw[j], x);
-#pragma unroll
-        for (int q = 0; q < W; ++q) e[q] = ex2(arg_folded(x[q], K, tc.c_hi, tc.c_lo));
-        us[j] = unit_sum<W>(e);
-      }
-#pragma unroll
-      for (int st = 1; st < NV; st *= 2) {
-#pragma unroll
-        for (int j = 0; j + st < NV; j += 2 * st) us[j] += us[j + st];
-      }
-      const double S = block_sum1<NW>((double)us[0], sh.sum);
-      // to the shifted form, sum 2^((z - M) c): factor 2^(K - M c), one rounding
-      if (tid == 0) *out = Partial{M, 0, S * exp2(fma(-(double)M, tc.c, (double)K))};
-    } else {
-      // Extreme temperatures or logits: overflow-safe arguments, units re-read one at a time
-      // (cache hits) to keep this rare path out of the common path's registers.
-      double acc = 0.0;
-#pragma unroll 1
-      for (int j = 0; j < NV; ++j) {
-        const int32_t u = j * NT + tid;
-        if (u < nu) {
-          float x[W], e[W];
-          U::cvt(U::template load<false>(tile, u), x);
-#pragma unroll
-          for (int q = 0; q < W; ++q) e[q] = ex2(arg_shifted(x[q], M, tc.c_hi, tc.c_lo));
-          acc += (double)unit_sum<W>(e);
-        }
-      }
-      const double S = block_sum1<NW>(acc, sh.sum);
-      if (tid == 0) *out = Partial{M, 0, S};
-    }
-  } else {
-    // Greedy row: the lowest index holding the tile maximum; only threads whose own maximum
-    // equals it search their units.
-    int32_t ti = INT32_MAX;
-    if (tm == M) {
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        float x[W];
-        U::cvt(raw[j], x);
-        const int32_t u = j * NT + tid;
-#pragma unroll
-        for (int q = 0; q < W; ++q)
-          if (ti == INT32_MAX && u < nu && x[q] == M) ti = (int32_t)((lo / W + u) * W + q);
-      }
-    }
-    const int32_t bi = block_min1<NW>(ti, sh.idx);
-    if (tid == 0) *out = Partial{M, bi, 0.0};
-  }
+  load_tile<DT, VEC, NV>(tile, nu, raw);
+  tile_stats<DT, VEC, NV, false>(raw, tile, nu, lo, hi, T, T > 0.f ? xtok : -1,
+                                 P.parts + (int64_t)slot * P.nsplit + blockIdx.x, &P.rec[slot].z,
+                                 sh);
 }
 
 // ------------------------------------------------------------------ finishing a request
@@ -676,8 +769,9 @@ struct ReqLds {
 //     k_rowstats captured) and the first rejection by ballot + find-first-set.
 // Merged rows sit in L by row slot (target row r at r, draft row i at gamma + 1 + i).  With
 // `write`, the outputs and the row probes are written.  Ends with a barrier; the stop row is
-// in L.j.  Returns the request's temperature constant.
-template <int NT>
+// in L.j.  Returns the request's temperature constant.  SHARED: the partials and slot records
+// were written by other workgroups of the same launch.
+template <int NT, bool SHARED>
 __device__ TempConst finish_head(const Params &P, int32_t b, bool write, ReqLds &L,
                                  int64_t &dbase, int32_t &gb, bool &sampling) {
   constexpr int NW = NT / 64;
@@ -703,8 +797,8 @@ __device__ TempConst finish_head(const Params &P, int32_t b, bool write, ReqLds 
   SlotRec rt = {};
   float zd = 0.f;
   if (wave == 0 && lane < P.gamma) {
-    rt = P.rec[slot0 + lane];
-    if (!P.greedy_all) zd = P.rec[slot0 + dslot + lane].z;
+    rt = get_rec<SHARED>(P.rec + slot0 + lane);
+    if (!P.greedy_all) zd = get_rec<SHARED>(P.rec + slot0 + dslot + lane).z;
   }
   Partial pv[G];
 #pragma unroll
@@ -713,7 +807,7 @@ __device__ TempConst finish_head(const Params &P, int32_t b, bool write, ReqLds 
     pv[q].m = -INFINITY;
     pv[q].idx = INT32_MAX;
     pv[q].s = 0.0;
-    if (k < P.spr && sl < P.nsplit) pv[q] = P.parts[(slot0 + k) * P.nsplit + sl];
+    if (k < P.spr && sl < P.nsplit) pv[q] = get_partial<SHARED>(P.parts + (slot0 + k) * P.nsplit + sl);
   }
   sampling = T > 0.f;
   const int64_t tbase = dbase + b;
@@ -731,7 +825,8 @@ __device__ TempConst finish_head(const Params &P, int32_t b, bool write, ReqLds 
         pv[q].m = -INFINITY;
         pv[q].idx = INT32_MAX;
         pv[q].s = 0.0;
-        if (k < P.spr && sl < P.nsplit) pv[q] = P.parts[(slot0 + k) * P.nsplit + sl];
+        if (k < P.spr && sl < P.nsplit)
+          pv[q] = get_partial<SHARED>(P.parts + (slot0 + k) * P.nsplit + sl);
       }
     }
 #pragma unroll
@@ -743,14 +838,14 @@ __device__ TempConst finish_head(const Params &P, int32_t b, bool write, ReqLds 
       if (sampling) {
         float m = live ? pv[q].m : -INFINITY;
         if (live)
-          for (int32_t p = sl + lp; p < P.nsplit; p += lp) m = fmaxf(m, rowp[p].m);
+          for (int32_t p = sl + lp; p < P.nsplit; p += lp) m = fmaxf(m, get_partial<SHARED>(rowp + p).m);
         for (int o = lp >> 1; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
         const float M = m;
         double f = 0.0;
         if (live) {
           if (pv[q].m != -INFINITY) f = pv[q].s * exp2(((double)pv[q].m - (double)M) * tc.c);
           for (int32_t p = sl + lp; p < P.nsplit; p += lp) {
-            const Partial o = rowp[p];
+            const Partial o = get_partial<SHARED>(rowp + p);
             if (o.m != -INFINITY) f += o.s * exp2(((double)o.m - (double)M) * tc.c);
           }
         }
@@ -763,7 +858,10 @@ __device__ TempConst finish_head(const Params &P, int32_t b, bool write, ReqLds 
         float bv = live ? pv[q].m : -INFINITY;
         int32_t bi = live ? pv[q].idx : INT32_MAX;
         if (live)
-          for (int32_t p = sl + lp; p < P.nsplit; p += lp) argmax_merge(bv, bi, rowp[p].m, rowp[p].idx);
+          for (int32_t p = sl + lp; p < P.nsplit; p += lp) {
+            const Partial o = get_partial<SHARED>(rowp + p);
+            argmax_merge(bv, bi, o.m, o.idx);
+          }
         for (int o = lp >> 1; o > 0; o >>= 1) {
           const float ov = __shfl_xor(bv, o);
           const int32_t oi = __shfl_xor(bi, o);
@@ -912,12 +1010,23 @@ __device__ void draw_token(const Params &P, int32_t b, const Stop &st, const dou
   const int64_t nchunks = (nunits + 63) / 64;
 
   // Each thread sums a contiguous run of chunks, a block scan places the runs, and the
-  // thread whose run crosses the target walks it.
+  // thread whose run crosses the target walks it.  Runs of up to kDrawKeep chunks (every
+  // vocabulary up to 128K units) stay in registers, so the walk needs no second round trip.
+  constexpr int kDrawKeep = 8;
   const int64_t per = (nchunks + NT - 1) / NT;
   const int64_t a = tid * per;
   const int64_t e_ = a + per < nchunks ? a + per : nchunks;
+  const bool kept = per <= kDrawKeep;  // uniform
+  double keep[kDrawKeep];
   double mine = 0.0;
-  for (int64_t c = a; c < e_; ++c) mine += share_load(&cs[c]);
+  if (kept) {
+#pragma unroll
+    for (int i = 0; i < kDrawKeep; ++i) keep[i] = a + i < e_ ? share_load(&cs[a + i]) : 0.0;
+#pragma unroll
+    for (int i = 0; i < kDrawKeep; ++i) mine += keep[i];
+  } else {
+    for (int64_t c = a; c < e_; ++c) mine += share_load(&cs[c]);
+  }
   double R;
   const double before = block_excl_scan<NW>(mine, D.shd, R);
   const double target = u * R;
@@ -932,17 +1041,36 @@ __device__ void draw_token(const Params &P, int32_t b, const Stop &st, const dou
   if (tid == pick) {
     double run = before;
     int64_t lastpos = -1;
-    for (int64_t c = a; c < e_; ++c) {
-      const double v = share_load(&cs[c]);
-      if (v > 0.0) {
-        lastpos = c;
-        if (first != INT32_MAX && run + v > target) {
-          D.c = (int32_t)c;
-          D.local = target - run;
-          break;
+    bool found = false;
+    if (kept) {
+#pragma unroll
+      for (int i = 0; i < kDrawKeep; ++i) {
+        const double v = keep[i];
+        if (!found && a + i < e_) {
+          if (v > 0.0) {
+            lastpos = a + i;
+            if (first != INT32_MAX && run + v > target) {
+              D.c = (int32_t)(a + i);
+              D.local = target - run;
+              found = true;
+            }
+          }
+          run += v;
         }
       }
-      run += v;
+    } else {
+      for (int64_t c = a; c < e_; ++c) {
+        const double v = share_load(&cs[c]);
+        if (v > 0.0) {
+          lastpos = c;
+          if (first != INT32_MAX && run + v > target) {
+            D.c = (int32_t)c;
+            D.local = target - run;
+            break;
+          }
+        }
+        run += v;
+      }
     }
     if (D.c < 0) {
       D.c = (int32_t)lastpos;
@@ -1019,7 +1147,7 @@ __global__ __launch_bounds__(kThreads) void k_finish(Params P) {
   int64_t dbase;
   int32_t gb;
   bool sampling;
-  const TempConst tc = finish_head<kThreads>(P, b, split == 0, L, dbase, gb, sampling);
+  const TempConst tc = finish_head<kThreads, false>(P, b, split == 0, L, dbase, gb, sampling);
   if (!sampling) return;
   const Stop st = make_stop(L, gb, P.gamma + 1, tc, dbase + b + L.j, dbase + L.j);
   const int64_t nunits = (P.V + W - 1) / W;
@@ -1034,6 +1162,138 @@ __global__ __launch_bounds__(kThreads) void k_finish(Params P) {
              (uint32_t)P.nslice - 1u;
   __syncthreads();
   if (!s_last) return;
+  draw_token<DT, VEC, kThreads>(P, b, st, cs, D);
+}
+
+// ------------------------------------------------------------------ k_onepass
+
+// The whole step in one launch, for calls whose workgroups can all be resident at once (the
+// host checks the device's capacity for this kernel).  Workgroup (request b, slice s),
+// blockIdx.x = b * nsplit + s, owns columns [s * split_len, (s + 1) * split_len) of every row of
+// its request, so a request's workgroups are few and only they meet:
+//  1. row statistics of its slice of each of the request's rows, as k_rowstats computes them
+//     (the next row's loads go out before the current row is reduced), handed over as
+//     device-scope atomic stores;
+//  2. it adds itself to the request's arrival counter.  A greedy request is finished by the
+//     last arrival (merge and comparisons, as k_finish).  The workgroups of a sampled request
+//     wait, polling, until all nsplit have arrived; each then merges and runs the accept tests
+//     (slice 0 writes the outputs), sums its slice of the stop row(s) into chunk sums, and adds
+//     itself to a second counter; the last one draws, as k_finish's last slice does.
+// The last user of each counter returns it to zero, so every call leaves them zeroed.  A wait
+// is bounded (kSpinLimit polls); a request whose workgroups never all arrive (only possible if
+// they could not all be resident) is reported with out_num_accepted = -1.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_onepass(Params P) {
+  using U = Unit<DT, VEC>;
+  using Store = typename U::Store;
+  constexpr int W = U::W;
+  constexpr int NV = int(kOneTileBytes / (DT == SPEC_F32 ? 4 : 2) / kThreads) / W;
+  static_assert(kThreads == kRsThreads, "tile_stats runs on a k_rowstats-sized workgroup");
+  __shared__ StatsLds sh;
+  __shared__ ReqLds L;
+  __shared__ DrawLds<kWaves> D;
+  __shared__ int32_t s_tok[SPEC_MAX_GAMMA];
+  __shared__ int32_t s_go;
+  const int tid = threadIdx.x;
+  const int32_t b = (int32_t)(blockIdx.x / (uint32_t)P.nsplit);
+  const int32_t split = (int32_t)(blockIdx.x - (uint32_t)b * (uint32_t)P.nsplit);
+  int64_t dbase;
+  int32_t gb;
+  float T;
+  request(P, b, dbase, gb, T);
+  const bool sampling = T > 0.f;
+  const int32_t nrows = gb + 1 + (sampling ? gb : 0);  // target rows 0..gb, then draft rows
+  const int64_t lo = (int64_t)split * P.split_len;
+  const int64_t hi = lo + P.split_len < P.V ? lo + P.split_len : P.V;
+  const int32_t nu = (int32_t)((hi - lo + W - 1) / W);
+  const int64_t slot0 = (int64_t)b * P.spr;
+  // row r of the loop: target row r (slot r) for r <= gb, else draft row r - gb - 1 (slot
+  // gamma + 1 + that)
+  auto tile_of = [&](int32_t r) -> const Store * {
+    const bool tgt = r <= gb;
+    const int64_t row = tgt ? dbase + b + r : dbase + (r - gb - 1);
+    return static_cast<const Store *>(row_ptr<DT>(tgt ? P.target : P.draft, row, P.V)) + lo / W;
+  };
+
+  typename U::Raw cur[NV], nxt[NV];
+  load_tile<DT, VEC, NV>(tile_of(0), nu, nxt);
+  // The draft tokens (and, from slice 0, the slot records of the target rows) go out with the
+  // first row's loads.
+  if (tid < gb) {
+    const int32_t x = P.tokens[dbase + tid];
+    s_tok[tid] = x;
+    if (split == 0) {
+      SlotRec *rec = P.rec + slot0 + tid;
+      put_u32<true>(&rec->tok, (uint32_t)x);
+      put_u32<true>(&rec->u, __float_as_uint(sampling ? P.uniforms[2 * (dbase + b + tid)] : 0.f));
+    }
+  }
+  __syncthreads();
+  for (int32_t r = 0; r < nrows; ++r) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) cur[j] = nxt[j];
+    if (r + 1 < nrows) load_tile<DT, VEC, NV>(tile_of(r + 1), nu, nxt);
+    const bool tgt = r <= gb;
+    const int32_t pos = tgt ? r : r - gb - 1;
+    const int32_t k = tgt ? r : P.gamma + 1 + pos;
+    const int32_t tok = sampling && pos < gb ? s_tok[pos] : -1;
+    tile_stats<DT, VEC, NV, true>(cur, tile_of(r), nu, lo, hi, T, tok,
+                                  P.parts + (slot0 + k) * P.nsplit + split, &P.rec[slot0 + k].z,
+                                  sh);
+  }
+
+  // Arrival: this workgroup's stores are complete before it counts itself in.
+  wait_memory();
+  __syncthreads();
+  const uint32_t n = (uint32_t)P.nsplit;
+  if (tid == 0) {
+    const uint32_t old =
+        __hip_atomic_fetch_add(&P.arrive[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int32_t go = old == n - 1u ? 2 : 1;  // 2: the last arrival
+    if (go == 1 && sampling) {
+      uint32_t spins = 0;
+      while (__hip_atomic_load(&P.arrive[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins == kSpinLimit) {
+          go = -1;
+          break;
+        }
+      }
+    }
+    s_go = go;
+  }
+  __syncthreads();
+  const int32_t go = s_go;
+  int64_t db;
+  int32_t g;
+  bool smp;
+  if (!sampling) {
+    if (go != 2) return;
+    if (tid == 0) __hip_atomic_store(&P.arrive[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    finish_head<kThreads, true>(P, b, true, L, db, g, smp);
+    return;
+  }
+  if (go < 0) {
+    if (tid == 0) P.out_n[b] = -1;
+    return;
+  }
+  const TempConst tc = finish_head<kThreads, true>(P, b, split == 0, L, db, g, smp);
+  const Stop st = make_stop(L, gb, P.gamma + 1, tc, dbase + b + L.j, dbase + L.j);
+  // This slice of the stop row(s): lo is a multiple of kOneAlign elements, so its first unit
+  // starts a 64-unit chunk.
+  double *cs = P.chunk_sums + (int64_t)b * P.chunk_stride;
+  stream_chunks<DT, VEC, kThreads, kFinRU>(P, st, lo / W, lo / W + nu, cs);
+  wait_memory();
+  __syncthreads();
+  if (tid == 0)
+    s_go = __hip_atomic_fetch_add(&P.odone[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           n - 1u;
+  __syncthreads();
+  if (!s_go) return;
+  if (tid == 0) {
+    __hip_atomic_store(&P.arrive[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&P.odone[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   draw_token<DT, VEC, kThreads>(P, b, st, cs, D);
 }
 
@@ -1248,9 +1508,11 @@ __global__ __launch_bounds__(kNgramPackThreads) void k_ngram_pack(NgramParams G)
 // ------------------------------------------------------------------ host side
 
 struct Plan {
-  int32_t spr, nsplit;
+  int32_t spr, nsplit;       // row slots per request; k_rowstats tiles per row
   int64_t split_len, chunk_stride;
-  size_t off_parts, off_rec, off_chunks, off_done, total;
+  int32_t one_nsplit;        // k_onepass workgroups per request; 0: the call cannot take it
+  int64_t one_split_len;
+  size_t off_sync, off_parts, off_rec, off_chunks, off_done, total;
 };
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -1275,10 +1537,27 @@ bool make_plan(int32_t B, int32_t gamma, int64_t V, int dtype, bool greedy, Plan
   }
   pl.nsplit = (int32_t)ceil_div(V, len);  // no empty slice
   pl.split_len = len;
+  // k_onepass: slices of whole kOneAlign blocks, at most kOneTileBytes of a row; when requests
+  // are few, enough slices for about kOneTargetWgs workgroups; at most kOneMaxSlices.
+  {
+    const int64_t least = ceil_div(V, kOneTileBytes / (dtype == SPEC_F32 ? 4 : 2));
+    int64_t want = ceil_div(kOneTargetWgs, bb);
+    const int64_t cap = ceil_div(V, kOneAlign);
+    if (want > cap) want = cap;
+    if (want > kOneMaxSlices) want = kOneMaxSlices;
+    if (want < least) want = least;
+    pl.one_split_len = ceil_div(ceil_div(V, want), kOneAlign) * kOneAlign;
+    const int64_t ns = ceil_div(V, pl.one_split_len);
+    pl.one_nsplit = ns <= kOneMaxSlices && bb <= kOneMaxB ? (int32_t)ns : 0;
+  }
+  const int64_t parts_split = pl.nsplit > pl.one_nsplit ? pl.nsplit : pl.one_nsplit;
   // Chunk sums of the stop rows; the element path (one element per unit) has the most chunks.
   pl.chunk_stride = ceil_div(V, kChunkUnits);
-  pl.off_parts = 0;
-  pl.off_rec = align_up((size_t)bb * pl.spr * pl.nsplit * sizeof(Partial));
+  // The one-launch counters sit first, at the same place and size for every call, so that
+  // calls of any shape find them as the last call left them: zero.
+  pl.off_sync = 0;
+  pl.off_parts = align_up(2 * (size_t)kOneMaxB * sizeof(uint32_t));
+  pl.off_rec = pl.off_parts + align_up((size_t)bb * pl.spr * parts_split * sizeof(Partial));
   pl.off_chunks = pl.off_rec + align_up((size_t)bb * pl.spr * sizeof(SlotRec));
   pl.off_done = pl.off_chunks +
                 (greedy ? 0 : align_up((size_t)bb * pl.chunk_stride * sizeof(double)));
@@ -1310,8 +1589,36 @@ int launch(K kernel, dim3 grid, int threads, const spec_probe *probe, int k, hip
              : SPEC_ERR_HIP;
 }
 
+// Workgroups of `kernel` (kThreads each) the current device holds at once; 0 if unknown.
+int resident_capacity(const void *kernel) {
+  int dev = 0, cus = 0, per = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kThreads, 0) != hipSuccess) {
+    (void)hipGetLastError();  // leave no error behind for the launch check
+    return 0;
+  }
+  return per * cus;
+}
+
 template <int DT, bool VEC>
 int run(Params P, const Plan &pl, const spec_probe *probe, hipStream_t s) {
+  // Two launches unless the probe asks for one.  On MI355X the one-launch path measured
+  // slower at every size tried (a handoff between workgroups inside a launch costs about as
+  // many dependent memory round trips as the kernel boundary it saves), so it is never the
+  // library's own choice.
+  const int path = probe ? probe->path : SPEC_PATH_AUTO;
+  if (path != SPEC_PATH_AUTO && path != SPEC_PATH_TWO && path != SPEC_PATH_ONE)
+    return SPEC_ERR_SHAPE;
+  if (path == SPEC_PATH_ONE) {
+    const int64_t grid = (int64_t)P.B * pl.one_nsplit;
+    if (pl.one_nsplit == 0 ||
+        grid > resident_capacity(reinterpret_cast<const void *>(k_onepass<DT, VEC>)))
+      return SPEC_ERR_SHAPE;
+    P.nsplit = pl.one_nsplit;
+    P.split_len = pl.one_split_len;
+    return launch(k_onepass<DT, VEC>, dim3((uint32_t)grid), kThreads, probe, 0, s, P);
+  }
   const int64_t slots = (int64_t)P.B * pl.spr;
   const uint32_t gy = (uint32_t)(slots < kMaxGridY ? slots : kMaxGridY);
   const uint32_t gz = (uint32_t)ceil_div(slots, gy);
@@ -1348,6 +1655,8 @@ int setup(Params &P, const Plan &pl, void *workspace, size_t workspace_bytes) {
   P.parts = reinterpret_cast<Partial *>(ws + pl.off_parts);
   P.rec = reinterpret_cast<SlotRec *>(ws + pl.off_rec);
   P.done = reinterpret_cast<uint32_t *>(ws + pl.off_done);
+  P.arrive = reinterpret_cast<uint32_t *>(ws + pl.off_sync);
+  P.odone = P.arrive + kOneMaxB;
   P.chunk_sums = reinterpret_cast<double *>(ws + pl.off_chunks);
   P.chunk_stride = pl.chunk_stride;
   P.spr = pl.spr;

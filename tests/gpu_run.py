@@ -11,7 +11,7 @@ def to_device(w, device="cuda"):
     return workloads.to_torch(w, device)
 
 
-def launches(w, *, greedy: bool = False) -> int:
+def launches(w, *, greedy: bool = False, path: int = sv.SPEC_PATH_AUTO) -> int:
     """Kernel launches one call makes on workload ``w``, read from the probe's event slots
     (the library records events 2k / 2k+1 around its k-th launch)."""
     import ctypes
@@ -27,7 +27,7 @@ def launches(w, *, greedy: bool = False) -> int:
     ws = sv.alloc_workspace(w.B, w.gamma, w.V, code)
     out = torch.empty(w.R_t, dtype=torch.int32, device="cuda")
     nacc = torch.empty(w.B, dtype=torch.int32, device="cuda")
-    pr = sv.make_probe(events=evs)
+    pr = sv.make_probe(events=evs, path=path)
     if greedy:
         sv.spec_verify_greedy(d["target"], d["tokens"], w.gamma, out, nacc, ws,
                               cu_draft=d["cu"], probe=pr)
@@ -49,8 +49,9 @@ def launches(w, *, greedy: bool = False) -> int:
 
 
 def run(w, *, greedy: bool = False, probe: bool = True, dev=None, workspace=None,
-        sync: bool = True) -> dict:
-    """Verify workload ``w`` on the GPU; returns numpy outputs (and probe arrays)."""
+        sync: bool = True, path: int = sv.SPEC_PATH_AUTO) -> dict:
+    """Verify workload ``w`` on the GPU; returns numpy outputs (and probe arrays).  ``path``
+    selects the launch path (one of sv.SPEC_PATH_*; the library's choice by default)."""
     import torch
     d = to_device(w) if dev is None else dev
     code = sv.SPEC_F32 if w.dtype == "f32" else sv.SPEC_BF16
@@ -69,7 +70,9 @@ def run(w, *, greedy: bool = False, probe: bool = True, dev=None, workspace=None
                        row_max_d=torch.full((w.R_d,), np.nan, **f32),
                        row_sum_d=torch.full((w.R_d,), np.nan, **f64),
                        resid_mass=torch.full((w.B,), np.nan, **f64))
-        pr = sv.make_probe(**tensors)
+        pr = sv.make_probe(**tensors, path=path)
+    elif path != sv.SPEC_PATH_AUTO:
+        pr = sv.make_probe(path=path)
     if greedy:
         sv.spec_verify_greedy(d["target"], d["tokens"], w.gamma, out, nacc, ws,
                               cu_draft=d["cu"], probe=pr)

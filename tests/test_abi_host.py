@@ -141,3 +141,18 @@ def test_ngram_outputs_may_be_null_when_nothing_is_proposed():
 
 def test_ngram_with_no_requests_is_a_no_op():
     assert _ngram(B=0, seq=None, ln=None, counts=None, dense=None) == 0
+
+
+@pytest.mark.parametrize("path", [-1, 3, 7])
+def test_unknown_launch_path_is_a_shape_error(path):
+    # the probe's launch-path field is checked on the host, before anything is enqueued
+    pr = sv.make_probe(path=path)
+    assert _sample(probe=ctypes.byref(pr)) == -2
+    assert _greedy(probe=ctypes.byref(pr)) == -2
+
+
+def test_workspace_keeps_a_fixed_counter_region():
+    # the one-launch counters (2 x 2048 uint32) come first in every workspace, so sizes grow
+    # by that much at least and any shape finds them at offset 0
+    assert sv.spec_verify_workspace_size(1, 0, 1, sv.SPEC_F32) >= 16384
+    assert sv.spec_verify_workspace_size(1, 0, 1, sv.SPEC_F32) < 16384 + 4096

@@ -1,23 +1,28 @@
 """HIP path vs the fp64 oracle on the same seeded inputs, through the C ABI.
 
 Small shapes and the five workloads at full size (in the launch configuration the benchmark
-times) run the oracle on every request.
+times) run the oracle on every request.  Calls small enough for the one-launch path run on
+both launch paths.
 """
 import numpy as np
 import pytest
 
 import oracle
+import speculative_sampling_verification_spec_amd as sv
 import workloads
 from tests import parity
 from tests.gpu_run import launches, run, to_device
 
 pytestmark = pytest.mark.gpu
 
+AUTO, TWO, ONE = sv.SPEC_PATH_AUTO, sv.SPEC_PATH_TWO, sv.SPEC_PATH_ONE
+PATHS = pytest.mark.parametrize("path", [TWO, ONE], ids=["two", "one"])
 
-def _both(w, greedy=False, requests=None):
-    print(f"[gpu] {w.name} B={w.B} gamma={w.gamma} V={w.V} {w.dtype} greedy={greedy}",
-          flush=True)
-    g = run(w, greedy=greedy)
+
+def _both(w, greedy=False, requests=None, path=AUTO):
+    print(f"[gpu] {w.name} B={w.B} gamma={w.gamma} V={w.V} {w.dtype} greedy={greedy} "
+          f"path={path}", flush=True)
+    g = run(w, greedy=greedy, path=path)
     o = oracle.verify(w, requests=requests, greedy=greedy)
     rep = parity.compare(w, g, o, requests=requests, greedy_call=greedy)
     print(f"[gpu]   {rep}", flush=True)
@@ -39,28 +44,31 @@ SMALL = [
 ]
 
 
+@PATHS
 @pytest.mark.parametrize("B,gamma,V,dtype,ragged,temps", SMALL)
-def test_small_shapes_match_oracle(B, gamma, V, dtype, ragged, temps):
+def test_small_shapes_match_oracle(B, gamma, V, dtype, ragged, temps, path):
     if temps == "mixed":
         temps = np.where(np.arange(B) % 3 == 0, 0.0, np.linspace(0.2, 1.5, B))
     w = workloads.small(B=B, gamma=gamma, V=V, dtype=dtype, seed=B * 1000 + V, ragged=ragged,
                         temperatures=temps, draft_sigma=0.8)
-    _both(w)
+    _both(w, path=path)
 
 
+@PATHS
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("V", [64, 5000, 40000])
-def test_greedy_entry_point_matches_oracle(dtype, V):
+def test_greedy_entry_point_matches_oracle(dtype, V, path):
     w = workloads.small(B=11, gamma=6, V=V, dtype=dtype, seed=V, ragged=True,
                         temperatures=0.0, draft_sigma=0.3)
-    _both(w, greedy=True)
-    _both(w.as_greedy(), greedy=False)   # T = 0 rows inside the sampling entry point
+    _both(w, greedy=True, path=path)
+    _both(w.as_greedy(), greedy=False, path=path)   # T = 0 rows inside the sampling entry point
 
 
-def test_many_requests_peaked_rows():
+@PATHS
+def test_many_requests_peaked_rows(path):
     w = workloads.small(B=96, gamma=4, V=8192, dtype="bf16", seed=77, temperatures=0.7,
                         target_sigma=3.0, draft_sigma=1.0, peaks=5)
-    _, _, rep = _both(w)
+    _, _, rep = _both(w, path=path)
     assert rep["ambiguous"] <= 0.1 * rep["sampled"]
 
 
@@ -83,20 +91,60 @@ def test_long_rows_with_multi_tile_slices():
     (1, 1, 65_536, "f32"),       # one request: its slices alone make the grid
 ])
 def test_sliced_finish(B, gamma, V, dtype):
-    # every call is two launches: row statistics, then k_finish over (slice, request), whose
-    # last slice per request draws; the number of slices follows B and V
+    # two launches: row statistics, then k_finish over (slice, request), whose last slice per
+    # request draws; the number of slices follows B and V
     temps = np.where(np.arange(B) % 4 == 1, 0.0, np.linspace(0.4, 1.4, B))
     w = workloads.small(B=B, gamma=gamma, V=V, dtype=dtype, seed=B * 7 + V, ragged=True,
                         temperatures=temps, draft_sigma=0.9)
-    assert launches(w) == 2
-    _both(w)
-    assert launches(w, greedy=True) == 2
-    _both(w, greedy=True)
+    assert launches(w, path=TWO) == 2
+    _both(w, path=TWO)
+    assert launches(w, greedy=True, path=TWO) == 2
+    _both(w, greedy=True, path=TWO)
+
+
+@pytest.mark.parametrize("B,gamma,V,dtype", [
+    (300, 2, 4096, "bf16"),      # many requests: one slice each
+    (5, 3, 16, "f32"),           # a single chunk
+    (1, 1, 65_536, "f32"),       # one request: 32 slices
+    (1000, 1, 512, "bf16"),      # a thousand one-slice requests
+    (3, 2, 100_001, "f32"),      # the element path, 28 slices
+])
+def test_one_launch_slices(B, gamma, V, dtype):
+    # one launch: workgroup (request, slice) over every row of its request; the workgroups of
+    # a request meet on its arrival counter, the last one to finish its chunk sums draws
+    temps = np.where(np.arange(B) % 4 == 1, 0.0, np.linspace(0.4, 1.4, B))
+    w = workloads.small(B=B, gamma=gamma, V=V, dtype=dtype, seed=B * 11 + V, ragged=True,
+                        temperatures=temps, draft_sigma=0.9)
+    assert launches(w, path=ONE) == 1
+    _both(w, path=ONE)
+    assert launches(w, greedy=True, path=ONE) == 1
+    _both(w, greedy=True, path=ONE)
+
+
+def test_one_launch_refuses_calls_it_cannot_take():
+    # rows over 32 one-launch slices: asking for one launch is a shape error, nothing runs
+    w = workloads.small(B=2, gamma=3, V=300_000, dtype="bf16", seed=5, temperatures=0.8)
+    with pytest.raises(sv.SpecVerifyError) as e:
+        run(w, path=ONE)
+    assert e.value.code == -2
+    assert launches(w) == 2     # the library's own choice takes two
+
+
+@pytest.mark.parametrize("B", [8, 64])
+@PATHS
+def test_single_draft_small_batch(B, path):
+    # one draft per request (the single-token MTP case of the Perplexity page, "Planification
+    # MTP pour un jeton unique"), small decode batches at the full Llama-3 vocabulary: both
+    # launch paths, the one-launch path being the latency-bound case's
+    temps = np.where(np.arange(B) % 5 == 0, 0.0, np.linspace(0.5, 1.1, B))
+    w = workloads.small(B=B, gamma=1, V=128256, dtype="bf16", seed=60 + B, temperatures=temps,
+                        target_sigma=3.0, draft_sigma=1.0)
+    assert launches(w, path=path) == (1 if path == ONE else 2)
+    _both(w, path=path)
 
 
 def test_single_draft_decode_batch():
-    # one draft per request (the single-token MTP case of the Perplexity page, "Planification
-    # MTP pour un jeton unique"): 2 target rows + 1 draft row per request, full vocabulary
+    # the same with 256 requests (too many workgroups for one launch: two)
     temps = np.where(np.arange(256) % 5 == 0, 0.0, np.linspace(0.5, 1.1, 256))
     w = workloads.small(B=256, gamma=1, V=128256, dtype="bf16", seed=61, temperatures=temps,
                         target_sigma=3.0, draft_sigma=1.0)
@@ -105,7 +153,8 @@ def test_single_draft_decode_batch():
 
 # ----------------------------------------------------------------------- edge cases
 
-def test_p_equal_q_accepts_everything_on_gpu():
+@PATHS
+def test_p_equal_q_accepts_everything_on_gpu(path):
     w = workloads.small(B=40, gamma=8, V=3000, dtype="bf16", seed=5, temperatures=0.9,
                         ragged=True)
     for b, (tb, db, g) in enumerate(zip(w.target_base, w.draft_base, w.gammas)):
@@ -113,29 +162,31 @@ def test_p_equal_q_accepts_everything_on_gpu():
     rng = np.random.default_rng(9)
     w.draft_tokens[:] = workloads.draw_draft_tokens(workloads.decode(w.draft, "bf16"), 0.9, rng)
     w.uniforms[:, 0] = np.float32(np.nextafter(np.float32(1), np.float32(0)))
-    g = run(w)
+    g = run(w, path=path)
     np.testing.assert_array_equal(g["num_accepted"], w.gammas)
-    _both(w)
+    _both(w, path=path)
 
 
-def test_gamma_zero_and_max_gamma():
+@PATHS
+def test_gamma_zero_and_max_gamma(path):
     w0 = workloads.small(B=4, gamma=1, V=500, seed=1)
     # one unused draft row and token keep the (never read) pointers non-NULL
     w0 = workloads.Workload("gamma0", "f32", 4, 0, 500, w0.target[:4].copy(),
                             np.zeros((1, 500), np.float32), np.zeros(1, np.int32),
                             w0.uniforms[:4].copy(), np.array([1.0, 0.0, 0.5, 2.0], np.float32))
-    _both(w0)
+    _both(w0, path=path)
     w64 = workloads.small(B=3, gamma=64, V=300, dtype="f32", seed=2, temperatures=1.0,
                           draft_sigma=0.05)
-    g, o, _ = _both(w64)
+    g, o, _ = _both(w64, path=path)
     assert (o["num_accepted"] >= 32).any()  # long accepted runs exercise the lane loop
     wg = workloads.small(B=3, gamma=64, V=300, dtype="bf16", seed=3, temperatures=0.0,
                          draft_sigma=0.0)
-    g, o, _ = _both(wg, greedy=True)
+    g, o, _ = _both(wg, greedy=True, path=path)
     assert (o["num_accepted"] == 64).all()   # drafts are the target argmax: all accepted
 
 
-def test_ragged_with_empty_requests():
+@PATHS
+def test_ragged_with_empty_requests(path):
     base = workloads.small(B=6, gamma=5, V=777, dtype="bf16", seed=4, ragged=True,
                            temperatures=np.array([0.8, 0, 1.1, 0.5, 0, 0.3]))
     # make requests 1 and 4 have no drafts: drop their draft rows and rebuild CSR
@@ -152,43 +203,48 @@ def test_ragged_with_empty_requests():
                            base.target[keep_t].copy(), base.draft[keep_d].copy(),
                            base.draft_tokens[keep_d].copy(), base.uniforms[keep_t].copy(),
                            base.temperatures.copy(), cu)
-    _both(w)
+    _both(w, path=path)
 
 
-def test_single_token_vocabulary():
+@PATHS
+def test_single_token_vocabulary(path):
     w = workloads.small(B=5, gamma=3, V=1, dtype="f32", seed=6, ragged=True,
                         temperatures=np.array([1.0, 0.0, 0.5, 0.0, 2.0]))
-    g, o, _ = _both(w)
+    g, o, _ = _both(w, path=path)
     np.testing.assert_array_equal(g["num_accepted"], w.gammas)
 
 
-def test_extreme_temperatures():
+@PATHS
+def test_extreme_temperatures(path):
     # tiny and huge T; with logits near +-10 the smaller temperatures take the row
     # statistics' overflow-safe exponent form, the others the two-FMA form
     temps = np.array([1e-30, 1e-6, 1e-3, 50.0, 1e4, 0.0], dtype=np.float32)
     w = workloads.small(B=6, gamma=4, V=2048, dtype="bf16", seed=8, temperatures=temps)
-    _both(w)
+    _both(w, path=path)
 
 
-def test_large_logits():
+@PATHS
+def test_large_logits(path):
     # logits of magnitude ~1e4 at T = 1: |max| c is above the two-FMA limit
     w = workloads.small(B=4, gamma=3, V=3000, dtype="f32", seed=9, temperatures=1.0,
                         target_sigma=1.0, draft_sigma=0.5)
     w.target += np.float32(-2.0e4)
     w.draft += np.float32(-2.0e4)
-    _both(w)
+    _both(w, path=path)
 
 
-def test_draft_ids_outside_vocabulary():
+@PATHS
+def test_draft_ids_outside_vocabulary(path):
     w = workloads.small(B=6, gamma=4, V=900, dtype="f32", seed=10,
                         temperatures=np.array([1.0, 0.0, 0.6, 0.0, 1.2, 0.9]))
     w.draft_tokens[1::3] = 900
     w.draft_tokens[2::5] = -3
-    _both(w)
-    _both(w, greedy=True)
+    _both(w, path=path)
+    _both(w, greedy=True, path=path)
 
 
-def test_unaligned_rows_take_the_element_path():
+@PATHS
+def test_unaligned_rows_take_the_element_path(path):
     # a row stride that is not a multiple of 16 bytes, and a base offset by one element
     import torch
     w = workloads.small(B=4, gamma=3, V=1001, dtype="bf16", seed=12, temperatures=0.9)
@@ -199,18 +255,18 @@ def test_unaligned_rows_take_the_element_path():
         buf = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
         buf[1:] = t.reshape(-1)
         d[k] = buf[1:].view_as(t)
-    g = run(w, dev=d)
+    g = run(w, dev=d, path=path)
     parity.compare(w, g, o)
 
 
-@pytest.mark.parametrize("V", [256, 200_000])
-def test_bonus_fallback_when_residual_is_empty(V):
+@pytest.mark.parametrize("V,path", [(256, TWO), (256, ONE), (200_000, TWO), (100_000, ONE)])
+def test_bonus_fallback_when_residual_is_empty(V, path):
     # p = q at a rejected position (uniform at its upper edge): the residual is empty and
     # the draw falls back to p, as the oracle does (both finishing paths).
     w = workloads.small(B=3, gamma=2, V=V, dtype="f32", seed=13, temperatures=1.0)
     w.draft[:] = w.target[np.concatenate([[0, 1], [3, 4], [6, 7]])]
     w.uniforms[:, 0] = 1.0
-    g, o, _ = _both(w)
+    g, o, _ = _both(w, path=path)
     assert (o["fallback"] == 1).all()
     sure = o["cdf_gap"] >= parity.AMBIGUOUS
     assert sure.any()
@@ -221,22 +277,25 @@ def test_bonus_fallback_when_residual_is_empty(V):
 
 # ----------------------------------------------------------------------- the workloads
 
-def test_workload1_tiny_sampling():
+@PATHS
+def test_workload1_tiny_sampling(path):
     w = workloads.config(1)
-    g, o, rep = _both(w)
+    g, o, rep = _both(w, path=path)
     assert rep["ambiguous"] == 0
 
 
-def test_workload2_greedy_bit_exact():
+@PATHS
+def test_workload2_greedy_bit_exact(path):
     w = workloads.config(2)
-    g, o, _ = _both(w, greedy=True)
-    g2, _, _ = _both(w, greedy=False)    # the same step through the mixed entry point
+    g, o, _ = _both(w, greedy=True, path=path)
+    g2, _, _ = _both(w, greedy=False, path=path)    # the same step through the mixed entry point
     np.testing.assert_array_equal(g["out_tokens"], g2["out_tokens"])
 
 
-def test_workload3_llama3_vocab_sampling():
+@PATHS
+def test_workload3_llama3_vocab_sampling(path):
     w = workloads.config(3)
-    _, _, rep = _both(w)
+    _, _, rep = _both(w, path=path)
     assert rep["sampled"] == 64
 
 
@@ -252,33 +311,38 @@ def test_workload5_full_size_every_request():
     assert rep["greedy"] == 102 and rep["sampled"] == 410
 
 
-def test_repeated_calls_are_bit_identical():
+@PATHS
+def test_repeated_calls_are_bit_identical(path):
     w = workloads.small(B=32, gamma=6, V=20000, dtype="bf16", seed=14, ragged=True,
                         temperatures=np.linspace(0, 1.2, 32))
     d = to_device(w)
-    a = run(w, dev=d)
-    b = run(w, dev=d)
+    a = run(w, dev=d, path=path)
+    b = run(w, dev=d, path=path)
     for k in a:
         np.testing.assert_array_equal(a[k], b[k])
 
 
-def test_one_workspace_across_shapes_needs_no_clearing():
-    # the workspace holds the per-request arrival counters of k_finish; it is filled with
-    # 0xff once and then reused by calls of different sizes, which must still match the oracle
+def test_one_workspace_across_shapes_and_paths():
+    # one workspace, zero in its first 16 KiB (the one-launch counters) and 0xff beyond, is
+    # reused by calls of different sizes on both launch paths, which must all match the
+    # oracle; every call leaves the counters at zero
     import torch
-    import speculative_sampling_verification_spec_amd as sv
-    shapes = [(40, 5, 30000, "bf16"), (3, 8, 70001, "f32"), (64, 2, 4096, "bf16"),
-              (40, 5, 30000, "bf16")]
+    shapes = [(40, 5, 30000, "bf16", ONE), (3, 8, 70001, "f32", TWO), (64, 2, 4096, "bf16", ONE),
+              (40, 5, 30000, "bf16", TWO), (3, 8, 70001, "f32", ONE), (64, 2, 4096, "bf16", TWO),
+              (40, 5, 30000, "bf16", ONE)]
     need = max(sv.spec_verify_workspace_size(B, g, V, sv.SPEC_BF16 if dt == "bf16" else sv.SPEC_F32)
-               for B, g, V, dt in shapes)
+               for B, g, V, dt, _ in shapes)
     ws = torch.full((need,), 0xff, dtype=torch.uint8, device="cuda")
-    for i, (B, gamma, V, dtype) in enumerate(shapes):
+    ws[:16384] = 0
+    for i, (B, gamma, V, dtype, path) in enumerate(shapes):
         temps = np.where(np.arange(B) % 5 == 2, 0.0, np.linspace(0.5, 1.3, B))
         w = workloads.small(B=B, gamma=gamma, V=V, dtype=dtype, seed=300 + i, ragged=True,
                             temperatures=temps, draft_sigma=1.0)
-        print(f"[gpu] shared workspace call {i}: B={B} gamma={gamma} V={V} {dtype}", flush=True)
-        g = run(w, workspace=ws)
+        print(f"[gpu] shared workspace call {i}: B={B} gamma={gamma} V={V} {dtype} path={path}",
+              flush=True)
+        g = run(w, workspace=ws, path=path)
         parity.compare(w, g, oracle.verify(w))
+        assert int(ws[:16384].count_nonzero()) == 0
 
 
 def test_prepared_call_repeats_the_entry_point():
