@@ -136,6 +136,9 @@ def main():
                     help="only run the plain copy the byte counters are calibrated with")
     ap.add_argument("--path", choices=sorted(PATHS), default="auto",
                     help="launch path: the library's choice (auto), two launches, or one")
+    ap.add_argument("--single-draft", type=int, default=0, metavar="B",
+                    help="instead of a workload: a decode batch of B requests with one draft "
+                         "each (V = 128256 bf16, T = 0.7)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -154,7 +157,14 @@ def main():
         copy_calibration()
         return
     t_gen = time.perf_counter()
-    w = workloads.config(args.workload)
+    if args.single_draft > 0:
+        B = args.single_draft
+        w = workloads.generate(name=f"single-draft decode batch B={B} V=128256 bf16 T=0.7",
+                               B=B, V=128256, dtype="bf16", gammas=[1] * B, dense=True,
+                               target_sigma=3.0, draft_sigma=1.0, temperatures=0.7, seed=98)
+        args.workload = 0
+    else:
+        w = workloads.config(args.workload)
     print(f"[bench] generated workload {args.workload} in {time.perf_counter() - t_gen:.1f} s",
           file=sys.stderr, flush=True)
     nbytes = w.compulsory_bytes
@@ -251,7 +261,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: {w.name}", "B": w.B, "gamma_max": w.gamma,
+        "config": {"workload": f"{args.workload}: {w.name}" if args.workload else w.name,
+                   "B": w.B, "gamma_max": w.gamma,
                    "V": w.V, "logit_dtype": w.dtype, "positions_per_step": positions,
                    "logit_bytes_per_step": nbytes, "input_copies": copies,
                    "launch_path": taken, "parallelism": "single GPU"},
