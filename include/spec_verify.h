@@ -85,7 +85,8 @@ enum {
  *                 the call's workgroups resident on the device at once (checked against the
  *                 device's capacity for the kernel).  A request whose workgroups do not all
  *                 arrive within a bounded wait (seconds; only if other work keeps them from
- *                 being resident) comes back with out_num_accepted = -1.
+ *                 being resident) comes back with out_num_accepted = -1, and the workspace
+ *                 must then be zero-filled again before its next use.
  *  SPEC_PATH_AUTO the library's choice, the default: two launches.  On MI355X the one-launch
  *                 path measured slower at every size tried, small batches included: the
  *                 handoff between workgroups inside the launch costs about as many dependent
