@@ -81,8 +81,9 @@ enum {
  *  SPEC_PATH_ONE  one launch for small calls: each workgroup takes one column slice of every
  *                 row of its request, and the few workgroups of a request meet inside the
  *                 launch (device-scope atomics and bounded polling), so the call costs one
- *                 kernel boundary instead of two.  Requires B <= 2048, V <= 262144 and all of
- *                 the call's workgroups resident on the device at once (checked against the
+ *                 kernel boundary instead of two.  Requires B <= 2048, rows of at most 32
+ *                 slices of 16 KiB (V <= 262144 bf16, 131072 fp32) and all of the call's
+ *                 workgroups resident on the device at once (checked against the
  *                 device's capacity for the kernel).  A request whose workgroups do not all
  *                 arrive within a bounded wait (seconds; only if other work keeps them from
  *                 being resident) comes back with out_num_accepted = -1, and the workspace

@@ -31,6 +31,26 @@ def _close(a, b):
     return ok
 
 
+def _margins(orc, db, g, on):
+    """Oracle accept-test margins at the draft positions up to the oracle's stop row."""
+    last = min(on, g - 1)
+    return orc["margin"][db: db + last + 1] if g > 0 else np.array([])
+
+
+def _ambiguous(orc, b, margins) -> bool:
+    return bool((margins < AMBIGUOUS).any()) or orc["cdf_gap"][b] < AMBIGUOUS
+
+
+def ambiguous_requests(w, orc: dict) -> np.ndarray:
+    """Per request: sampled (T > 0) and, by the rule above, ambiguous."""
+    out = np.zeros(w.B, dtype=bool)
+    for b in range(w.B):
+        if w.temperatures[b] > 0:
+            g, db = int(w.gammas[b]), int(w.draft_base[b])
+            out[b] = _ambiguous(orc, b, _margins(orc, db, g, int(orc["num_accepted"][b])))
+    return out
+
+
 def compare(w, gpu: dict, orc: dict, requests=None, greedy_call: bool = False,
             probes: bool = True) -> dict:
     """Check ``gpu`` against ``orc`` on ``requests`` (default all); returns a report and
@@ -71,9 +91,8 @@ def compare(w, gpu: dict, orc: dict, requests=None, greedy_call: bool = False,
                     errors.append(f"req {b}: row max differs")
             continue
         rep["sampled"] += 1
-        last = min(on, g - 1)
-        margins = orc["margin"][db: db + last + 1] if g > 0 else np.array([])
-        ambiguous = bool((margins < AMBIGUOUS).any()) or orc["cdf_gap"][b] < AMBIGUOUS
+        margins = _margins(orc, db, g, on)
+        ambiguous = _ambiguous(orc, b, margins)
         if ambiguous:
             rep["ambiguous"] += 1
             rep["ambiguous_matched"] += int(equal)

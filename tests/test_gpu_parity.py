@@ -151,6 +151,42 @@ def test_single_draft_decode_batch():
     _both(w)
 
 
+def _random_case(i):
+    """Seeded random call: B, gamma, V, dtype, dense or ragged, a mix of greedy and sampled
+    requests, target/draft closeness and temperatures over a wide range."""
+    rng = np.random.default_rng(7000 + i)
+    dtype = "bf16" if rng.random() < 0.6 else "f32"
+    B = int(rng.integers(1, 48))
+    gamma = int(rng.integers(1, 11))
+    V = int(rng.choice([rng.integers(1, 600), rng.integers(600, 20000), rng.integers(20000, 130000)]))
+    temps = np.where(rng.random(B) < 0.25, 0.0, rng.uniform(0.05, 2.0, B))
+    return dict(B=B, gamma=gamma, V=V, dtype=dtype, seed=7000 + i, ragged=bool(rng.random() < 0.6),
+                temperatures=temps, target_sigma=float(rng.uniform(0.5, 4.0)),
+                draft_sigma=float(rng.uniform(0.05, 1.5)))
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_calls_on_both_paths(i):
+    # the same seeded call on both launch paths: each matches the oracle under the parity
+    # rules, and the two agree on every request the oracle does not mark ambiguous
+    kw = _random_case(i)
+    w = workloads.small(**kw)
+    o = oracle.verify(w)
+    res = {}
+    for path in (TWO, ONE):
+        print(f"[gpu] random call {i}: B={w.B} gamma={w.gamma} V={w.V} {w.dtype} path={path}",
+              flush=True)
+        g = run(w, path=path)
+        parity.compare(w, g, o)
+        res[path] = g
+    sure = ~parity.ambiguous_requests(w, o)
+    for b in np.flatnonzero(sure):
+        tb, gb = w.target_base[b], w.gammas[b]
+        np.testing.assert_array_equal(res[TWO]["out_tokens"][tb: tb + gb + 1],
+                                      res[ONE]["out_tokens"][tb: tb + gb + 1])
+    np.testing.assert_array_equal(res[TWO]["num_accepted"][sure], res[ONE]["num_accepted"][sure])
+
+
 # ----------------------------------------------------------------------- edge cases
 
 @PATHS
