@@ -1,7 +1,8 @@
 """Benchmark of the speculative-sampling verification step on one MI355X.
 
 One step = one call of spec_verify_sample over a whole batch (row statistics, accept tests,
-first-reject scan, residual mass, draw; greedy rows of the batch included).  Inputs are
+first-reject scan, residual mass, draw; greedy rows of the batch included), or of
+spec_verify_greedy for a workload whose requests are all greedy (workload 2).  Inputs are
 seeded synthetic workloads resident in HBM before timing; consecutive steps rotate over
 enough input copies (> 2 x the 256 MB last-level cache) that no step reads cache-hot logits.
 
@@ -30,8 +31,9 @@ sys.path.insert(0, str(ROOT))
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MALL_BYTES = 256 << 20          # last-level (Infinity) cache
 # launches of one call: row statistics, then accept tests + residual + draw (two-launch
-# path), or the whole step (one-launch path, small calls)
-KERNELS = {"two": ["k_rowstats", "k_finish"], "one": ["k_onepass"]}
+# path), or the whole step (one-launch path: k_greedy1 for greedy calls, k_onepass else)
+KERNELS = {"two": ["k_rowstats", "k_finish"], "one_greedy": ["k_greedy1"],
+           "one": ["k_onepass"]}
 PATHS = {"auto": 0, "two": 1, "one": 2}
 DEFAULT_WORKLOAD = 5
 WARMUP_SECONDS = 0.25
@@ -180,11 +182,18 @@ def main():
     hip = HipEvents()
     path = PATHS[args.path]
 
+    all_greedy = bool((w.temperatures == 0).all())  # the greedy entry point's workload
+
     def step(k, probe):
         probe = probe if probe is not None or path == 0 else sv.make_probe(path=path)
         d = inputs[k % copies]
-        sv.spec_verify_sample(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temps"],
-                              w.gamma, out, nacc, ws, cu_draft=d["cu"], probe=probe)
+        if all_greedy:
+            sv.spec_verify_greedy(d["target"], d["tokens"], w.gamma, out, nacc, ws,
+                                  cu_draft=d["cu"], probe=probe)
+        else:
+            sv.spec_verify_sample(d["target"], d["draft"], d["tokens"], d["uniforms"],
+                                  d["temps"], w.gamma, out, nacc, ws, cu_draft=d["cu"],
+                                  probe=probe)
 
     # Warm-up: W steps, continued until at least 0.25 s of sustained load has passed (the
     # GPU's clocks settle some milliseconds into a run).
@@ -201,9 +210,13 @@ def main():
     # (on this stack every recorded event leaves the GPU idle for several microseconds), and
     # each input copy's call marshalled once, as a serving loop would hold it.
     ctl = sv.make_probe(path=path) if path else None
-    calls = [sv.prepare_sample(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temps"],
-                               w.gamma, out, nacc, ws, cu_draft=d["cu"], probe=ctl)
-             for d in inputs]
+    if all_greedy:
+        calls = [sv.prepare_greedy(d["target"], d["tokens"], w.gamma, out, nacc, ws,
+                                   cu_draft=d["cu"], probe=ctl) for d in inputs]
+    else:
+        calls = [sv.prepare_sample(d["target"], d["draft"], d["tokens"], d["uniforms"],
+                                   d["temps"], w.gamma, out, nacc, ws, cu_draft=d["cu"], probe=ctl)
+                 for d in inputs]
     t0 = time.perf_counter()
     for k in range(args.steps):
         calls[k % copies]()
@@ -223,7 +236,7 @@ def main():
         hip.hip.hipGetLastError()
         taken = "one"
     hip.destroy(evs)
-    kernels = KERNELS[taken]
+    kernels = KERNELS["one_greedy" if taken == "one" and all_greedy else taken]
 
     # Timed region B: the same steps again with per-kernel durations from events that each
     # kernel's dispatch records (probe events) on the stream it runs on.
@@ -265,6 +278,7 @@ def main():
                    "B": w.B, "gamma_max": w.gamma,
                    "V": w.V, "logit_dtype": w.dtype, "positions_per_step": positions,
                    "logit_bytes_per_step": nbytes, "input_copies": copies,
+                   "entry_point": "spec_verify_greedy" if all_greedy else "spec_verify_sample",
                    "launch_path": taken, "parallelism": "single GPU"},
         "logit_GB_per_s": round(logit_gbps, 1),
         "hbm_frac": round(logit_gbps / HBM_PEAK_GBPS, 4),

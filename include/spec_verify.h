@@ -78,20 +78,21 @@ enum {
  * How a verification call is launched (spec_probe.path).  Both ways compute the same step.
  *  SPEC_PATH_TWO  two launches: a row-statistics stream over every needed logit, then one that
  *                 merges, tests, sums the stop rows and draws.  Any size.
- *  SPEC_PATH_ONE  one launch for small calls: each workgroup takes one column slice of every
- *                 row of its request, and the few workgroups of a request meet inside the
- *                 launch (device-scope atomics and bounded polling), so the call costs one
- *                 kernel boundary instead of two.  Requires B <= 2048, rows of at most 32
- *                 slices of 16 KiB (V <= 262144 bf16, 131072 fp32) and all of the call's
- *                 workgroups resident on the device at once (checked against the
- *                 device's capacity for the kernel).  A request whose workgroups do not all
- *                 arrive within a bounded wait (seconds; only if other work keeps them from
- *                 being resident) comes back with out_num_accepted = -1, and the workspace
- *                 must then be zero-filled again before its next use.
- *  SPEC_PATH_AUTO the library's choice, the default: two launches.  On MI355X the one-launch
- *                 path measured slower at every size tried, small batches included: the
- *                 handoff between workgroups inside the launch costs about as many dependent
- *                 memory round trips as the kernel boundary it removes.
+ *  SPEC_PATH_ONE  one launch.  Greedy calls (spec_verify_greedy): row-statistics tiles whose
+ *                 last arrival per request merges and writes the request's outputs; B <= 2048.
+ *                 Sampling calls: each workgroup takes one column slice of every row of its
+ *                 request, and the few workgroups of a request meet inside the launch
+ *                 (device-scope atomics and bounded polling); B <= 2048, rows of at most 32
+ *                 slices of 16 KiB (V <= 262144 bf16, 131072 fp32), and all of the call's
+ *                 workgroups resident on the device at once (at most three quarters of the
+ *                 device's capacity for the kernel).  A request whose workgroups do not all arrive
+ *                 within a bounded wait (seconds; only if other work keeps them from being
+ *                 resident) comes back with out_num_accepted = -1, and the workspace must then
+ *                 be zero-filled again before its next use.
+ *  SPEC_PATH_AUTO the library's choice, the default: one launch where it measured faster on
+ *                 MI355X (greedy calls of at most 2048 row tiles of 16K elements; sampling
+ *                 calls with gamma <= 1, 16-byte aligned rows and at most 512 one-launch
+ *                 workgroups), else two.
  */
 #define SPEC_PATH_AUTO 0
 #define SPEC_PATH_TWO 1
@@ -139,9 +140,9 @@ typedef struct spec_probe {
  *  out_num_accepted [B] int32      n_b in [0, gamma_b]; the step emits n_b + 1 tokens
  *  workspace      device scratch of at least spec_verify_workspace_size(B, gamma, V, dtype)
  *                 bytes, 256-byte aligned, zero-filled before its first use; every call
- *                 leaves it ready for the next, of any shape.  Its first 16 KiB hold the
- *                 one-launch path's per-request counters, which each call returns to zero;
- *                 the rest needs no initial contents
+ *                 leaves it ready for the next, of any shape.  Its first 512 KiB hold the
+ *                 one-launch path's per-request counters (one per 128-byte line), which each
+ *                 call returns to zero; the rest needs no initial contents
  *  probe          NULL, or diagnostics as above
  *  stream         hipStream_t
  *

@@ -19,6 +19,9 @@ SPEC_MAX_GAMMA = 64
 SPEC_NGRAM_MAX_N = 64
 SPEC_OK = 0
 SPEC_PATH_AUTO, SPEC_PATH_TWO, SPEC_PATH_ONE = 0, 1, 2
+# the workspace's leading counter region (2 x 2048 counters, one per 128-byte line), which
+# must be zero before a workspace's first use and which every call leaves at zero
+COUNTER_BYTES = 2 * 2048 * 128
 
 _lib = None
 

@@ -72,6 +72,8 @@ constexpr int64_t kOneAlign = 512;           // one-launch slices: whole chunks 
 constexpr int kOneMaxSlices = 32;            // one-launch workgroups per request, at most
 constexpr int kOneTargetWgs = 256;           // one-launch grid aimed for when rows are few
 constexpr int kOneMaxB = 2048;               // requests the one-launch counters cover
+constexpr int kCounterStride = 32;           // one counter per 128-byte line: atomics on a line
+                                             // serialise, so requests must not share one
 constexpr uint32_t kSpinLimit = 1u << 22;    // polls before a one-launch workgroup stops waiting
 constexpr int64_t kMaxV = int64_t(1) << 24;
 constexpr double kLog2e = 1.4426950408889634074;
@@ -123,8 +125,10 @@ struct Params {
   SlotRec *rec;             // [B][spr] per row slot: logit at the draft token, token, uniform
   double *chunk_sums;       // [B][chunk_stride] residual sums per 64-unit chunk
   int64_t chunk_stride;
-  uint32_t *done;           // [B] k_finish slices of each request finished (k_rowstats clears)
-  uint32_t *arrive, *odone; // [kOneMaxB] one-launch counters: zero before and after every call
+  uint32_t *done;           // k_finish slices of request b finished, at [b * kCounterStride]
+                            // (k_rowstats clears it)
+  uint32_t *arrive, *odone; // one-launch counters, request b's at [b * kCounterStride]: zero
+                            // before and after every call
   int32_t nslice;           // k_finish workgroups per request
   int64_t slice_units;      // stop-row units per k_finish workgroup (a multiple of 64)
   int32_t spr;              // row slots per request: 2*gamma+1 (sample) or gamma+1 (greedy)
@@ -666,7 +670,7 @@ __global__ __launch_bounds__(kRsThreads) void k_rowstats(Params P) {
   }
   // k_finish counts its workgroups per request from zero: the first tile of the request's
   // first target row (present in every request) clears the counter for it.
-  if (k == 0 && blockIdx.x == 0 && threadIdx.x == 0) P.done[b] = 0u;
+  if (k == 0 && blockIdx.x == 0 && threadIdx.x == 0) P.done[b * kCounterStride] = 0u;
   const int64_t lo = (int64_t)blockIdx.x * P.split_len;
   const int64_t hi = lo + P.split_len < P.V ? lo + P.split_len : P.V;
   const Store *tile = static_cast<const Store *>(row_ptr<DT>(base, row, P.V)) + lo / W;
@@ -772,7 +776,7 @@ struct ReqLds {
 // in L.j.  Returns the request's temperature constant.  SHARED: the partials and slot records
 // were written by other workgroups of the same launch.
 template <int NT, bool SHARED>
-__device__ TempConst finish_head(const Params &P, int32_t b, bool write, ReqLds &L,
+__device__ __forceinline__ TempConst finish_head(const Params &P, int32_t b, bool write, ReqLds &L,
                                  int64_t &dbase, int32_t &gb, bool &sampling) {
   constexpr int NW = NT / 64;
   constexpr int G = 4;  // rounds of row slots whose partials are loaded at once
@@ -997,7 +1001,8 @@ struct DrawLds {
 // a block scan over the chunk sums picks the chunk holding u * R, a wavefront scan over its
 // 64 units picks the unit, and a walk over the unit's elements gives the token.
 template <int DT, bool VEC, int NT>
-__device__ void draw_token(const Params &P, int32_t b, const Stop &st, const double *cs,
+__device__ __forceinline__ void draw_token(const Params &P, int32_t b, const Stop &st,
+                                           const double *cs,
                            DrawLds<NT / 64> &D) {
   using U = Unit<DT, VEC>;
   using Store = typename U::Store;
@@ -1159,11 +1164,68 @@ __global__ __launch_bounds__(kThreads) void k_finish(Params P) {
   wait_memory();
   __syncthreads();
   if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(&P.done[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+    s_last = __hip_atomic_fetch_add(&P.done[b * kCounterStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
              (uint32_t)P.nslice - 1u;
   __syncthreads();
   if (!s_last) return;
   draw_token<DT, VEC, kThreads>(P, b, st, cs, D);
+}
+
+// ------------------------------------------------------------------ k_greedy1
+
+// A greedy call (spec_verify_greedy) in one launch.  Workgroups (tile, row slot) as k_rowstats,
+// target rows only.  Each hands its (max, lowest argmax) partial over with device-scope atomic
+// stores, waits for them to complete and adds itself to its request's arrival counter; the
+// last arrival of a request merges the request's partials and writes its outputs, as k_finish's
+// slice 0 does.  No workgroup waits for another, so any grid works; the last arrival returns
+// the counter to zero.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kRsThreads) void k_greedy1(Params P) {
+  using U = Unit<DT, VEC>;
+  using Store = typename U::Store;
+  constexpr int W = U::W;
+  constexpr int NV = int(kTileElems / kRsThreads) / W;
+  __shared__ StatsLds sh;
+  __shared__ ReqLds L;
+  __shared__ int32_t s_last;
+  const int tid = threadIdx.x;
+  const uint32_t slot = blockIdx.y + blockIdx.z * gridDim.y;
+  const uint32_t spr = (uint32_t)P.spr;
+  if (slot >= (uint32_t)P.B * spr) return;
+  const int32_t b = (int32_t)(slot / spr);
+  const int32_t k = (int32_t)(slot - (uint32_t)b * spr);
+  int64_t dbase;
+  int32_t gb;
+  float T;
+  request(P, b, dbase, gb, T);
+  if (k > gb) return;
+  if (k < gb && blockIdx.x == 0 && tid == 0) {
+    put_u32<true>(&P.rec[slot].tok, (uint32_t)P.tokens[dbase + k]);
+    put_u32<true>(&P.rec[slot].u, 0u);
+  }
+  const int64_t lo = (int64_t)blockIdx.x * P.split_len;
+  const int64_t hi = lo + P.split_len < P.V ? lo + P.split_len : P.V;
+  const Store *tile =
+      static_cast<const Store *>(row_ptr<DT>(P.target, dbase + b + k, P.V)) + lo / W;
+  const int32_t nu = (int32_t)((hi - lo + W - 1) / W);
+  typename U::Raw raw[NV];
+  load_tile<DT, VEC, NV>(tile, nu, raw);
+  tile_stats<DT, VEC, NV, true>(raw, tile, nu, lo, hi, 0.f, -1,
+                                P.parts + (int64_t)slot * P.nsplit + blockIdx.x, &P.rec[slot].z,
+                                sh);
+  wait_memory();
+  __syncthreads();
+  const uint32_t n = (uint32_t)(gb + 1) * (uint32_t)P.nsplit;  // tiles of the request
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(&P.arrive[b * kCounterStride], 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) == n - 1u;
+  __syncthreads();
+  if (!s_last) return;
+  if (tid == 0) __hip_atomic_store(&P.arrive[b * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  int64_t db;
+  int32_t g;
+  bool smp;
+  finish_head<kRsThreads, true>(P, b, true, L, db, g, smp);
 }
 
 // ------------------------------------------------------------------ k_onepass
@@ -1173,8 +1235,7 @@ __global__ __launch_bounds__(kThreads) void k_finish(Params P) {
 // blockIdx.x = b * nsplit + s, owns columns [s * split_len, (s + 1) * split_len) of every row of
 // its request, so a request's workgroups are few and only they meet:
 //  1. row statistics of its slice of each of the request's rows, as k_rowstats computes them
-//     (the next row's loads go out before the current row is reduced), handed over as
-//     device-scope atomic stores;
+//     (three rows' loads in flight), handed over as device-scope atomic stores;
 //  2. it adds itself to the request's arrival counter.  A greedy request is finished by the
 //     last arrival (merge and comparisons, as k_finish).  The workgroups of a sampled request
 //     wait, polling, until all nsplit have arrived; each then merges and runs the accept tests
@@ -1184,7 +1245,8 @@ __global__ __launch_bounds__(kThreads) void k_finish(Params P) {
 // is bounded (kSpinLimit polls); a request whose workgroups never all arrive (only possible if
 // they could not all be resident) is reported with out_num_accepted = -1.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_onepass(Params P) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_onepass(
+    Params P) {
   using U = Unit<DT, VEC>;
   using Store = typename U::Store;
   constexpr int W = U::W;
@@ -1216,10 +1278,14 @@ __global__ __launch_bounds__(kThreads) void k_onepass(Params P) {
     return static_cast<const Store *>(row_ptr<DT>(tgt ? P.target : P.draft, row, P.V)) + lo / W;
   };
 
-  typename U::Raw cur[NV], nxt[NV];
-  load_tile<DT, VEC, NV>(tile_of(0), nu, nxt);
+  // Rows go through a ring of three register tiles: three rows' loads are in flight before
+  // the first is reduced, and each reduced row's tile is refilled with the row three ahead.
+  typename U::Raw t0[NV], t1[NV], t2[NV];
+  load_tile<DT, VEC, NV>(tile_of(0), nu, t0);
+  if (1 < nrows) load_tile<DT, VEC, NV>(tile_of(1), nu, t1);
+  if (2 < nrows) load_tile<DT, VEC, NV>(tile_of(2), nu, t2);
   // The draft tokens (and, from slice 0, the slot records of the target rows) go out with the
-  // first row's loads.
+  // first rows' loads.
   if (tid < gb) {
     const int32_t x = P.tokens[dbase + tid];
     s_tok[tid] = x;
@@ -1230,17 +1296,21 @@ __global__ __launch_bounds__(kThreads) void k_onepass(Params P) {
     }
   }
   __syncthreads();
-  for (int32_t r = 0; r < nrows; ++r) {
-#pragma unroll
-    for (int j = 0; j < NV; ++j) cur[j] = nxt[j];
-    if (r + 1 < nrows) load_tile<DT, VEC, NV>(tile_of(r + 1), nu, nxt);
+  // Statistics of loop row r from its tile, then the tile is refilled with row r + 3.
+  auto row_stats = [&](int32_t r, typename U::Raw(&t)[NV]) __attribute__((always_inline)) {
     const bool tgt = r <= gb;
     const int32_t pos = tgt ? r : r - gb - 1;
     const int32_t k = tgt ? r : P.gamma + 1 + pos;
     const int32_t tok = sampling && pos < gb ? s_tok[pos] : -1;
-    tile_stats<DT, VEC, NV, true>(cur, tile_of(r), nu, lo, hi, T, tok,
+    tile_stats<DT, VEC, NV, true>(t, tile_of(r), nu, lo, hi, T, tok,
                                   P.parts + (slot0 + k) * P.nsplit + split, &P.rec[slot0 + k].z,
                                   sh);
+    if (r + 3 < nrows) load_tile<DT, VEC, NV>(tile_of(r + 3), nu, t);
+  };
+  for (int32_t r = 0; r < nrows; r += 3) {  // uniform across the workgroup
+    row_stats(r, t0);
+    if (r + 1 < nrows) row_stats(r + 1, t1);
+    if (r + 2 < nrows) row_stats(r + 2, t2);
   }
 
   // Arrival: this workgroup's stores are complete before it counts itself in.
@@ -1249,11 +1319,11 @@ __global__ __launch_bounds__(kThreads) void k_onepass(Params P) {
   const uint32_t n = (uint32_t)P.nsplit;
   if (tid == 0) {
     const uint32_t old =
-        __hip_atomic_fetch_add(&P.arrive[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(&P.arrive[b * kCounterStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int32_t go = old == n - 1u ? 2 : 1;  // 2: the last arrival
     if (go == 1 && sampling) {
       uint32_t spins = 0;
-      while (__hip_atomic_load(&P.arrive[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n) {
+      while (__hip_atomic_load(&P.arrive[b * kCounterStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n) {
         __builtin_amdgcn_s_sleep(1);
         if (++spins == kSpinLimit) {
           go = -1;
@@ -1265,20 +1335,19 @@ __global__ __launch_bounds__(kThreads) void k_onepass(Params P) {
   }
   __syncthreads();
   const int32_t go = s_go;
-  int64_t db;
-  int32_t g;
-  bool smp;
-  if (!sampling) {
-    if (go != 2) return;
-    if (tid == 0) __hip_atomic_store(&P.arrive[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    finish_head<kThreads, true>(P, b, true, L, db, g, smp);
-    return;
-  }
+  if (!sampling && go != 2) return;  // a greedy request: only its last arrival goes on
   if (go < 0) {
     if (tid == 0) P.out_n[b] = -1;
     return;
   }
-  const TempConst tc = finish_head<kThreads, true>(P, b, split == 0, L, db, g, smp);
+  if (!sampling && tid == 0)
+    __hip_atomic_store(&P.arrive[b * kCounterStride], 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  int64_t db;
+  int32_t g;
+  bool smp;
+  const TempConst tc = finish_head<kThreads, true>(P, b, !sampling || split == 0, L, db, g, smp);
+  if (!sampling) return;
   const Stop st = make_stop(L, gb, P.gamma + 1, tc, dbase + b + L.j, dbase + L.j);
   // This slice of the stop row(s): lo is a multiple of kOneAlign elements, so its first unit
   // starts a 64-unit chunk.
@@ -1287,13 +1356,13 @@ __global__ __launch_bounds__(kThreads) void k_onepass(Params P) {
   wait_memory();
   __syncthreads();
   if (tid == 0)
-    s_go = __hip_atomic_fetch_add(&P.odone[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+    s_go = __hip_atomic_fetch_add(&P.odone[b * kCounterStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
            n - 1u;
   __syncthreads();
   if (!s_go) return;
   if (tid == 0) {
-    __hip_atomic_store(&P.arrive[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&P.odone[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&P.arrive[b * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&P.odone[b * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   draw_token<DT, VEC, kThreads>(P, b, st, cs, D);
 }
@@ -1557,12 +1626,12 @@ bool make_plan(int32_t B, int32_t gamma, int64_t V, int dtype, bool greedy, Plan
   // The one-launch counters sit first, at the same place and size for every call, so that
   // calls of any shape find them as the last call left them: zero.
   pl.off_sync = 0;
-  pl.off_parts = align_up(2 * (size_t)kOneMaxB * sizeof(uint32_t));
+  pl.off_parts = align_up(2 * (size_t)kOneMaxB * kCounterStride * sizeof(uint32_t));
   pl.off_rec = pl.off_parts + align_up((size_t)bb * pl.spr * parts_split * sizeof(Partial));
   pl.off_chunks = pl.off_rec + align_up((size_t)bb * pl.spr * sizeof(SlotRec));
   pl.off_done = pl.off_chunks +
                 (greedy ? 0 : align_up((size_t)bb * pl.chunk_stride * sizeof(double)));
-  pl.total = pl.off_done + align_up((size_t)bb * sizeof(uint32_t));
+  pl.total = pl.off_done + align_up((size_t)bb * kCounterStride * sizeof(uint32_t));
   return true;
 }
 
@@ -1602,23 +1671,52 @@ int resident_capacity(const void *kernel) {
   return per * cus;
 }
 
+// The library's own choice of one launch, where it measured faster on MI355X:
+//  - greedy calls of at most kOneGreedyTiles row tiles (one resident wave of k_greedy1);
+//  - sampling calls with at most one draft per request (three rows) and at most
+//    kOneSingleDraftGrid k_onepass workgroups.
+// Elsewhere two launches measured faster or equal (the one-launch workgroup reduces its rows
+// one after another).  Rows that are not 16-byte aligned take two launches too (the
+// one-launch kernel's element-path variant spills registers).
+constexpr int64_t kOneGreedyTiles = 2048;
+constexpr int64_t kOneSingleDraftGrid = 512;
+
 template <int DT, bool VEC>
 int run(Params P, const Plan &pl, const spec_probe *probe, hipStream_t s) {
-  // Two launches unless the probe asks for one.  On MI355X the one-launch path measured
-  // slower at every size tried (a handoff between workgroups inside a launch costs about as
-  // many dependent memory round trips as the kernel boundary it saves), so it is never the
-  // library's own choice.
-  const int path = probe ? probe->path : SPEC_PATH_AUTO;
-  if (path != SPEC_PATH_AUTO && path != SPEC_PATH_TWO && path != SPEC_PATH_ONE)
+  const int asked = probe ? probe->path : SPEC_PATH_AUTO;
+  if (asked != SPEC_PATH_AUTO && asked != SPEC_PATH_TWO && asked != SPEC_PATH_ONE)
     return SPEC_ERR_SHAPE;
+  const int64_t tiles = (int64_t)P.B * pl.spr * ceil_div(P.V, kTileElems);
+  int path = asked;
+  if (path == SPEC_PATH_AUTO) {
+    const bool one = P.B <= kOneMaxB &&
+                     (P.greedy_all ? tiles <= kOneGreedyTiles
+                                   : VEC && P.gamma <= 1 && pl.one_nsplit > 0 &&
+                                         (int64_t)P.B * pl.one_nsplit <= kOneSingleDraftGrid);
+    path = one ? SPEC_PATH_ONE : SPEC_PATH_TWO;
+  }
+  if (path == SPEC_PATH_ONE && P.greedy_all) {
+    // greedy: row-statistics tiles whose last arrival per request finishes it
+    if (P.B > kOneMaxB) return SPEC_ERR_SHAPE;
+    const int64_t slots = (int64_t)P.B * pl.spr;
+    const uint32_t gy = (uint32_t)(slots < kMaxGridY ? slots : kMaxGridY);
+    const uint32_t gz = (uint32_t)ceil_div(slots, gy);
+    P.split_len = kTileElems;
+    P.nsplit = (int32_t)ceil_div(P.V, kTileElems);
+    return launch(k_greedy1<DT, VEC>, dim3((uint32_t)P.nsplit, gy, gz), kRsThreads, probe, 0, s,
+                  P);
+  }
   if (path == SPEC_PATH_ONE) {
+    // every polling workgroup needs its siblings resident: keep a quarter of the device's
+    // capacity for this kernel spare
     const int64_t grid = (int64_t)P.B * pl.one_nsplit;
-    if (pl.one_nsplit == 0 ||
-        grid > resident_capacity(reinterpret_cast<const void *>(k_onepass<DT, VEC>)))
-      return SPEC_ERR_SHAPE;
-    P.nsplit = pl.one_nsplit;
-    P.split_len = pl.one_split_len;
-    return launch(k_onepass<DT, VEC>, dim3((uint32_t)grid), kThreads, probe, 0, s, P);
+    const int64_t cap = resident_capacity(reinterpret_cast<const void *>(k_onepass<DT, VEC>));
+    if (pl.one_nsplit > 0 && grid <= cap * 3 / 4) {
+      P.nsplit = pl.one_nsplit;
+      P.split_len = pl.one_split_len;
+      return launch(k_onepass<DT, VEC>, dim3((uint32_t)grid), kThreads, probe, 0, s, P);
+    }
+    if (asked == SPEC_PATH_ONE) return SPEC_ERR_SHAPE;
   }
   const int64_t slots = (int64_t)P.B * pl.spr;
   const uint32_t gy = (uint32_t)(slots < kMaxGridY ? slots : kMaxGridY);
@@ -1657,7 +1755,7 @@ int setup(Params &P, const Plan &pl, void *workspace, size_t workspace_bytes) {
   P.rec = reinterpret_cast<SlotRec *>(ws + pl.off_rec);
   P.done = reinterpret_cast<uint32_t *>(ws + pl.off_done);
   P.arrive = reinterpret_cast<uint32_t *>(ws + pl.off_sync);
-  P.odone = P.arrive + kOneMaxB;
+  P.odone = P.arrive + (size_t)kOneMaxB * kCounterStride;
   P.chunk_sums = reinterpret_cast<double *>(ws + pl.off_chunks);
   P.chunk_stride = pl.chunk_stride;
   P.spr = pl.spr;

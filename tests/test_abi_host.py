@@ -152,7 +152,7 @@ def test_unknown_launch_path_is_a_shape_error(path):
 
 
 def test_workspace_keeps_a_fixed_counter_region():
-    # the one-launch counters (2 x 2048 uint32) come first in every workspace, so sizes grow
-    # by that much at least and any shape finds them at offset 0
-    assert sv.spec_verify_workspace_size(1, 0, 1, sv.SPEC_F32) >= 16384
-    assert sv.spec_verify_workspace_size(1, 0, 1, sv.SPEC_F32) < 16384 + 4096
+    # the one-launch counters (2 x 2048, one per 128-byte line) come first in every workspace,
+    # so sizes grow by that much at least and any shape finds them at offset 0
+    assert sv.spec_verify_workspace_size(1, 0, 1, sv.SPEC_F32) >= sv.COUNTER_BYTES
+    assert sv.spec_verify_workspace_size(1, 0, 1, sv.SPEC_F32) < sv.COUNTER_BYTES + 4096

@@ -106,7 +106,7 @@ def test_sliced_finish(B, gamma, V, dtype):
     (300, 2, 4096, "bf16"),      # many requests: one slice each
     (5, 3, 16, "f32"),           # a single chunk
     (1, 1, 65_536, "f32"),       # one request: 32 slices
-    (1000, 1, 512, "bf16"),      # a thousand one-slice requests
+    (600, 1, 512, "bf16"),       # six hundred one-slice requests
     (3, 2, 100_001, "f32"),      # the element path, 28 slices
 ])
 def test_one_launch_slices(B, gamma, V, dtype):
@@ -130,7 +130,7 @@ def test_one_launch_refuses_calls_it_cannot_take():
     assert launches(w) == 2     # the library's own choice takes two
 
 
-@pytest.mark.parametrize("B", [8, 64])
+@pytest.mark.parametrize("B", [8, 32])
 @PATHS
 def test_single_draft_small_batch(B, path):
     # one draft per request (the single-token MTP case of the Perplexity page, "Planification
@@ -328,10 +328,11 @@ def test_workload2_greedy_bit_exact(path):
     np.testing.assert_array_equal(g["out_tokens"], g2["out_tokens"])
 
 
-@PATHS
-def test_workload3_llama3_vocab_sampling(path):
+def test_workload3_llama3_vocab_sampling():
+    # (its 1024 one-launch workgroups exceed three quarters of the device's capacity for that
+    # kernel, so it takes two launches only)
     w = workloads.config(3)
-    _, _, rep = _both(w, path=path)
+    _, _, rep = _both(w)
     assert rep["sampled"] == 64
 
 
@@ -359,7 +360,7 @@ def test_repeated_calls_are_bit_identical(path):
 
 
 def test_one_workspace_across_shapes_and_paths():
-    # one workspace, zero in its first 16 KiB (the one-launch counters) and 0xff beyond, is
+    # one workspace, zero in its counter region (the one-launch counters) and 0xff beyond, is
     # reused by calls of different sizes on both launch paths, which must all match the
     # oracle; every call leaves the counters at zero
     import torch
@@ -369,7 +370,7 @@ def test_one_workspace_across_shapes_and_paths():
     need = max(sv.spec_verify_workspace_size(B, g, V, sv.SPEC_BF16 if dt == "bf16" else sv.SPEC_F32)
                for B, g, V, dt, _ in shapes)
     ws = torch.full((need,), 0xff, dtype=torch.uint8, device="cuda")
-    ws[:16384] = 0
+    ws[:sv.COUNTER_BYTES] = 0
     for i, (B, gamma, V, dtype, path) in enumerate(shapes):
         temps = np.where(np.arange(B) % 5 == 2, 0.0, np.linspace(0.5, 1.3, B))
         w = workloads.small(B=B, gamma=gamma, V=V, dtype=dtype, seed=300 + i, ragged=True,
@@ -378,7 +379,7 @@ def test_one_workspace_across_shapes_and_paths():
               flush=True)
         g = run(w, workspace=ws, path=path)
         parity.compare(w, g, oracle.verify(w))
-        assert int(ws[:16384].count_nonzero()) == 0
+        assert int(ws[:sv.COUNTER_BYTES].count_nonzero()) == 0
 
 
 def test_prepared_call_repeats_the_entry_point():
