@@ -951,8 +951,8 @@ __device__ __forceinline__ Stop make_stop(const ReqLds &L, int32_t gb, int32_t d
 }
 
 // Step 3: units [ub, ub_end) of the stop row(s), NT * RU units per pass with all loads of a
-// pass in flight (nontemporal: the rows are read once more only at the drawn chunk); one fp64
-// sum per 64-unit chunk (one wavefront-wide load) into cs.  ub is a
+// pass in flight (ordinary loads: nontemporal ones here measured a slower row-statistics stream
+// in the next call); one fp64 sum per 64-unit chunk (one wavefront-wide load) into cs.  ub is a
 // multiple of 64 units, so every chunk is summed by one wavefront.
 template <int DT, bool VEC, int NT, int RU>
 __device__ __forceinline__ void stream_chunks(const Params &P, const Stop &st, int64_t ub,
@@ -969,8 +969,8 @@ __device__ __forceinline__ void stream_chunks(const Params &P, const Stop &st, i
 #pragma unroll
     for (int q = 0; q < RU; ++q) {
       const int64_t u = ub + q * NT + tid;
-      rt[q] = u < ub_end ? U::template load<true>(tr, u) : U::filler();
-      rd[q] = resid && u < ub_end ? U::template load<true>(dr, u) : U::filler();
+      rt[q] = u < ub_end ? U::template load<false>(tr, u) : U::filler();
+      rd[q] = resid && u < ub_end ? U::template load<false>(dr, u) : U::filler();
     }
 #pragma unroll
     for (int q = 0; q < RU; ++q) {
