@@ -87,6 +87,49 @@ def traffic_for_current_kernel(kernel: str, workload: int):
     return rec
 
 
+def context_figures():
+    """Context beside the 8 TB/s denominator, from the reference kernels of libspecbench.so on
+    the current stream: the GPU time of one empty launch back to back, and the rate of a plain
+    read stream (16-byte nontemporal loads) over 1 GiB buffers alternated beyond the
+    last-level cache."""
+    import torch
+    L = ctypes.CDLL(str(ROOT / "speculative_sampling_verification_spec_amd" / "libspecbench.so"))
+    L.spec_bench_empty.argtypes = [ctypes.c_int, ctypes.c_void_p]
+    L.spec_bench_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        e0.record()
+        for _ in range(reps):
+            if fn() != 0:
+                raise RuntimeError("reference kernel launch failed")
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps  # ms
+
+    n = 2000
+    timed(lambda: L.spec_bench_empty(200, stream), 2)
+    empty_us = timed(lambda: L.spec_bench_empty(n, stream), 1) * 1e3 / n
+    nbytes = COPY_BYTES
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(3)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    k = [0]
+
+    def read():
+        k[0] += 1
+        return L.spec_bench_read(ctypes.c_void_p(bufs[k[0] % 3].data_ptr()), nbytes,
+                                 ctypes.c_void_p(sink.data_ptr()), stream)
+
+    timed(read, 6)
+    ms = min(timed(read, 9) for _ in range(3))
+    del bufs
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"empty_launch_us": round(empty_us, 2), "read_stream_GB_per_s": round(gbps, 1),
+            "read_stream_frac": round(gbps / HBM_PEAK_GBPS, 4), "read_stream_bytes": nbytes}
+
+
 def copy_calibration():
     """A plain device-to-device copy of COPY_BYTES, the reference the HBM byte counters
     (FETCH_SIZE, WRITE_SIZE) are scaled by."""
@@ -252,6 +295,7 @@ def main():
                   for i, name in enumerate(kernels)}
     hip.destroy(evs)
     per_kernel_us = {name: round(float(d.mean()), 2) for name, d in per_kernel.items()}
+    step_kernels = sum(per_kernel.values())  # per step: the call's kernels back to back
     # the dominant kernel: the row-statistics stream, or the one launch that does everything
     rs_all = per_kernel[kernels[0]]
     rs_us = float(rs_all.mean())
@@ -283,6 +327,8 @@ def main():
         "logit_GB_per_s": round(logit_gbps, 1),
         "hbm_frac": round(logit_gbps / HBM_PEAK_GBPS, 4),
         "kernel_us": per_kernel_us,
+        "step_kernel_us_p10_p50_p90": [round(float(np.percentile(step_kernels, q)), 1)
+                                       for q in (10, 50, 90)],
         "roofline": {"bound": "hbm", "kernel": kernels[0], "kernel_us": round(rs_us, 2),
                      "kernel_us_p10_p50_p90": [round(float(np.percentile(rs_all, q)), 1)
                                                for q in (10, 50, 90)],
@@ -292,6 +338,7 @@ def main():
                      "traffic": None if traffic is None else traffic["hbm_bytes_per_launch"]},
         "cpu_baseline": None,
     }
+    result["context"] = context_figures()
     result["commit"] = time_commit(sv, w, out, nacc, d=inputs[0], steps=args.steps)
     result["ngram"] = time_ngram(sv, steps=args.steps)
     if not args.no_cpu_baseline:

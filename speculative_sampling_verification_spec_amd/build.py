@@ -10,6 +10,9 @@ PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 SRC = PKG / "csrc" / "spec_verify.hip"
 LIB = PKG / "libspecverify.so"
+# reference kernels for the benchmark's context figures (empty launch, plain read stream)
+BENCH_SRC = PKG / "csrc" / "bench_context.hip"
+BENCH_LIB = PKG / "libspecbench.so"
 INCLUDE = ROOT / "include"
 
 HIPCC_FLAGS = [
@@ -27,14 +30,21 @@ def hipcc() -> str:
     return path
 
 
-def build(extra_flags=(), out: Path | None = None) -> Path:
-    """Always recompiles; writes atomically so a running process never sees half a file."""
-    out = LIB if out is None else Path(out)
+def _compile(src: Path, out: Path, extra_flags=()) -> Path:
     tmp = out.with_name(out.name + ".tmp")
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, f"-I{INCLUDE}", str(SRC), "-o", str(tmp)]
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, f"-I{INCLUDE}", str(src), "-o", str(tmp)]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
+
+
+def build(extra_flags=(), out: Path | None = None) -> Path:
+    """Always recompiles (the library, then the benchmark's reference kernels); writes
+    atomically so a running process never sees half a file."""
+    lib = _compile(SRC, LIB if out is None else Path(out), extra_flags)
+    if out is None:
+        _compile(BENCH_SRC, BENCH_LIB, extra_flags)
+    return lib
 
 
 if __name__ == "__main__":
