@@ -159,8 +159,8 @@ int spec_verify_sample(const void *target_logits, const void *draft_logits, int 
  * spec_verify_greedy — the temperature-zero step (blent.ai page, "Pourquoi la qualité est
  * préservée"; wiki page, "実装上の注意"): draft i is accepted iff it equals the lowest-index
  * argmax of target row i; the argmax at the stop row is emitted.  Draft logits are not
- * taken.  Arguments as for spec_verify_sample; probe fields other than row_max_t and events
- * are ignored.
+ * taken.  Arguments as for spec_verify_sample; probe fields other than row_max_t, events and
+ * path are ignored.
  */
 int spec_verify_greedy(const void *target_logits, int dtype, const int32_t *draft_tokens,
                        int32_t B, int32_t gamma, const int32_t *cu_draft, int64_t V,

@@ -5,7 +5,8 @@
 // and emit a draw from max(p_j - q_j, 0) there, or from p_gamma when nothing was rejected;
 // at temperature zero, compare each draft with the target argmax instead.
 //
-// A verification call is two launches on the caller's stream, neither waiting for the host:
+// A verification call is two launches on the caller's stream, neither waiting for the host,
+// or one launch for small calls (below):
 //
 //  k_rowstats  The HBM-bound stream.  Every needed logit row is read exactly once, cut into
 //              16K-element tiles, one workgroup per (row slot, slice) on a 2-D grid; slots a
@@ -30,10 +31,18 @@
 //              ordered by a per-request arrival counter (which k_rowstats clears), so no cache
 //              writeback is needed inside the kernel.
 //
-// k_onepass, on request only (the probe's path field): the whole step in one launch for
-// calls whose workgroups all fit on the device at once; workgroup (request, column slice) over
-// every row of its request, the request's workgroups meeting on an arrival counter.  It gives
-// the same results and measured slower here, so two launches stay the default.
+// One launch, where it measured faster (small greedy calls, small single-draft batches), or
+// when the probe's path field asks for it:
+//
+//  k_greedy1   Greedy calls: k_rowstats' tiles over the target rows; the last tile of a
+//              request to finish merges the request's partials and writes its outputs.
+//
+//  k_onepass   Sampling calls whose workgroups all fit on the device at once: workgroup
+//              (request, column slice) over every row of its request; the request's
+//              workgroups meet on an arrival counter (bounded polling), then merge, test,
+//              stream their slices of the stop row(s) and draw as k_finish does.
+//
+// Per-request counters sit one per 128-byte line: atomics on one line serialise.
 //
 // After a call, for a serving loop that stays on the device: k_commit appends each
 // request's emitted tokens to its history and counts the step; k_ngram (+ k_ngram_pack)

@@ -121,6 +121,21 @@ def test_one_launch_slices(B, gamma, V, dtype):
     _both(w, greedy=True, path=ONE)
 
 
+def test_one_launch_greedy_at_the_counter_limit():
+    # 2048 greedy requests (the last counter of the one-launch region) and one more, which
+    # the one-launch path refuses and the library's own choice sends to two launches
+    w = workloads.small(B=2048, gamma=2, V=300, dtype="bf16", seed=41, temperatures=0.0,
+                        draft_sigma=0.2)
+    assert launches(w, greedy=True, path=ONE) == 1
+    _both(w, greedy=True, path=ONE)
+    w = workloads.small(B=2049, gamma=2, V=300, dtype="bf16", seed=42, temperatures=0.0,
+                        draft_sigma=0.2)
+    with pytest.raises(sv.SpecVerifyError):
+        run(w, greedy=True, path=ONE)
+    assert launches(w, greedy=True) == 2
+    _both(w, greedy=True)
+
+
 def test_one_launch_refuses_calls_it_cannot_take():
     # rows over 32 one-launch slices: asking for one launch is a shape error, nothing runs
     w = workloads.small(B=2, gamma=3, V=300_000, dtype="bf16", seed=5, temperatures=0.8)
