@@ -78,21 +78,20 @@ enum {
  * How a verification call is launched (spec_probe.path).  Both ways compute the same step.
  *  SPEC_PATH_TWO  two launches: a row-statistics stream over every needed logit, then one that
  *                 merges, tests, sums the stop rows and draws.  Any size.
- *  SPEC_PATH_ONE  one launch.  Greedy calls (spec_verify_greedy): row-statistics tiles whose
- *                 last arrival per request merges and writes the request's outputs; B <= 2048.
- *                 Sampling calls: each workgroup takes one column slice of every row of its
- *                 request, and the few workgroups of a request meet inside the launch
- *                 (device-scope atomics and bounded polling); B <= 2048, rows of at most 32
- *                 slices of 16 KiB (V <= 262144 bf16, 131072 fp32), and all of the call's
- *                 workgroups resident on the device at once (at most three quarters of the
- *                 device's capacity for the kernel).  A request whose workgroups do not all arrive
- *                 within a bounded wait (seconds; only if other work keeps them from being
- *                 resident) comes back with out_num_accepted = -1, and the workspace must then
- *                 be zero-filled again before its next use.
- *  SPEC_PATH_AUTO the library's choice, the default: one launch where it measured faster on
- *                 MI355X (greedy calls of at most 2048 row tiles of 16K elements; sampling
- *                 calls with gamma <= 1, 16-byte aligned rows and at most 512 one-launch
- *                 workgroups), else two.
+ *  SPEC_PATH_ONE  one launch, a workgroup per row tile as in the first of the two launches;
+ *                 B <= 2048.  Greedy calls (spec_verify_greedy): the last tile of a request to
+ *                 finish merges and writes the request's outputs.  Sampling calls: a request's
+ *                 tiles meet inside the launch (device-scope atomics and bounded polling),
+ *                 split its stop row(s) between them, and the last one draws; all of the
+ *                 call's workgroups (row slots x ceil(V / 16384)) must be resident on the
+ *                 device at once (at most three quarters of the device's capacity for the
+ *                 kernel).  A request whose workgroups do not all arrive within a bounded wait
+ *                 (seconds; only if other work keeps them from being resident) comes back with
+ *                 out_num_accepted = -1, and the workspace must then be zero-filled again
+ *                 before its next use.
+ *  SPEC_PATH_AUTO the library's choice, the default: one launch for calls of at most 2048 row
+ *                 tiles with 16-byte aligned rows that it can take, where it measured faster
+ *                 on MI355X; two launches otherwise.
  */
 #define SPEC_PATH_AUTO 0
 #define SPEC_PATH_TWO 1

@@ -31,16 +31,15 @@
 //              ordered by a per-request arrival counter (which k_rowstats clears), so no cache
 //              writeback is needed inside the kernel.
 //
-// One launch, where it measured faster (small greedy calls, small single-draft batches), or
-// when the probe's path field asks for it:
+// One launch for small calls, where it measured faster, or when the probe's path field asks:
 //
 //  k_greedy1   Greedy calls: k_rowstats' tiles over the target rows; the last tile of a
 //              request to finish merges the request's partials and writes its outputs.
 //
-//  k_onepass   Sampling calls whose workgroups all fit on the device at once: workgroup
-//              (request, column slice) over every row of its request; the request's
-//              workgroups meet on an arrival counter (bounded polling), then merge, test,
-//              stream their slices of the stop row(s) and draw as k_finish does.
+//  k_onepass   Sampling calls whose workgroups all fit on the device at once: k_rowstats'
+//              tiles over every row; the request's tiles meet on an arrival counter (bounded
+//              polling), then each merges and tests, sums its share of the stop row(s), and
+//              the last to finish draws, as k_finish does.
 //
 // Per-request counters sit one per 128-byte line: atomics on one line serialise.
 //
@@ -76,10 +75,6 @@ constexpr int kFinRU = 4;                    // k_finish: units per thread per r
 constexpr int kFinPassUnits = kThreads * kFinRU;  // k_finish: stop-row units per pass
 constexpr int kFinGrid = 1024;               // k_finish workgroups aimed for
 constexpr int kChunkUnits = 64;              // residual sums: one per 64 units (a wavefront load)
-constexpr int64_t kOneTileBytes = 16384;     // one-launch path: bytes per row per workgroup
-constexpr int64_t kOneAlign = 512;           // one-launch slices: whole chunks for every unit width
-constexpr int kOneMaxSlices = 32;            // one-launch workgroups per request, at most
-constexpr int kOneTargetWgs = 256;           // one-launch grid aimed for when rows are few
 constexpr int kOneMaxB = 2048;               // requests the one-launch counters cover
 constexpr int kCounterStride = 32;           // one counter per 128-byte line: atomics on a line
                                              // serialise, so requests must not share one
@@ -149,6 +144,8 @@ struct Params {
 };
 
 // ------------------------------------------------------------------ small helpers
+
+__device__ __forceinline__ int64_t ceil_div_dev(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 __device__ __forceinline__ void request(const Params &P, int32_t b, int64_t &dbase,
                                         int32_t &gb, float &T) {
@@ -1239,100 +1236,93 @@ __global__ __launch_bounds__(kRsThreads) void k_greedy1(Params P) {
 
 // ------------------------------------------------------------------ k_onepass
 
-// The whole step in one launch, for calls whose workgroups can all be resident at once (the
-// host checks the device's capacity for this kernel).  Workgroup (request b, slice s),
-// blockIdx.x = b * nsplit + s, owns columns [s * split_len, (s + 1) * split_len) of every row of
-// its request, so a request's workgroups are few and only they meet:
-//  1. row statistics of its slice of each of the request's rows, as k_rowstats computes them
-//     (three rows' loads in flight), handed over as device-scope atomic stores;
-//  2. it adds itself to the request's arrival counter.  A greedy request is finished by the
-//     last arrival (merge and comparisons, as k_finish).  The workgroups of a sampled request
-//     wait, polling, until all nsplit have arrived; each then merges and runs the accept tests
-//     (slice 0 writes the outputs), sums its slice of the stop row(s) into chunk sums, and adds
-//     itself to a second counter; the last one draws, as k_finish's last slice does.
-// The last user of each counter returns it to zero, so every call leaves them zeroed.  A wait
-// is bounded (kSpinLimit polls); a request whose workgroups never all arrive (only possible if
-// they could not all be resident) is reported with out_num_accepted = -1.
+// The whole step in one launch, for small calls.  Workgroups (tile, row slot) as k_rowstats:
+// each computes its tile's statistics, hands the partial over with device-scope atomic stores,
+// waits for them to complete and adds itself to its request's arrival counter.
+//  - A greedy request (T = 0) is finished by its last arrival: merge and comparisons, as
+//    k_finish's slice 0.  Nothing waits, so greedy calls take any grid.
+//  - The workgroups of a sampled request poll the counter (bounded: kSpinLimit polls) until
+//    all of the request's tiles are in, so the call's workgroups must all be resident at once
+//    (the host checks the device's capacity for this kernel).  Each then merges and tests (the
+//    request's first tile writes the outputs), sums its share of the stop row(s) into chunk
+//    sums, and adds itself to a second counter; the last one draws, as in k_finish.
+// The last user of each counter returns it to zero.  A request whose workgroups do not all
+// arrive within the bound (only possible if they could not all be resident) is reported with
+// out_num_accepted = -1.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_onepass(
-    Params P) {
+__global__ __launch_bounds__(kRsThreads) void k_onepass(Params P) {
   using U = Unit<DT, VEC>;
   using Store = typename U::Store;
   constexpr int W = U::W;
-  constexpr int NV = int(kOneTileBytes / (DT == SPEC_F32 ? 4 : 2) / kThreads) / W;
-  static_assert(kThreads == kRsThreads, "tile_stats runs on a k_rowstats-sized workgroup");
+  constexpr int NV = int(kTileElems / kRsThreads) / W;
+  static_assert(kThreads == kRsThreads, "the finishing steps run on a k_rowstats workgroup");
   __shared__ StatsLds sh;
   __shared__ ReqLds L;
   __shared__ DrawLds<kWaves> D;
-  __shared__ int32_t s_tok[SPEC_MAX_GAMMA];
   __shared__ int32_t s_go;
   const int tid = threadIdx.x;
-  const int32_t b = (int32_t)(blockIdx.x / (uint32_t)P.nsplit);
-  const int32_t split = (int32_t)(blockIdx.x - (uint32_t)b * (uint32_t)P.nsplit);
+  const uint32_t slot = blockIdx.y + blockIdx.z * gridDim.y;
+  const uint32_t spr = (uint32_t)P.spr;
+  if (slot >= (uint32_t)P.B * spr) return;
+  const int32_t b = (int32_t)(slot / spr);
+  const int32_t k = (int32_t)(slot - (uint32_t)b * spr);
   int64_t dbase;
   int32_t gb;
   float T;
   request(P, b, dbase, gb, T);
   const bool sampling = T > 0.f;
-  const int32_t nrows = gb + 1 + (sampling ? gb : 0);  // target rows 0..gb, then draft rows
-  const int64_t lo = (int64_t)split * P.split_len;
-  const int64_t hi = lo + P.split_len < P.V ? lo + P.split_len : P.V;
-  const int32_t nu = (int32_t)((hi - lo + W - 1) / W);
-  const int64_t slot0 = (int64_t)b * P.spr;
-  // row r of the loop: target row r (slot r) for r <= gb, else draft row r - gb - 1 (slot
-  // gamma + 1 + that)
-  auto tile_of = [&](int32_t r) -> const Store * {
-    const bool tgt = r <= gb;
-    const int64_t row = tgt ? dbase + b + r : dbase + (r - gb - 1);
-    return static_cast<const Store *>(row_ptr<DT>(tgt ? P.target : P.draft, row, P.V)) + lo / W;
-  };
-
-  // Rows go through a ring of three register tiles: three rows' loads are in flight before
-  // the first is reduced, and each reduced row's tile is refilled with the row three ahead.
-  typename U::Raw t0[NV], t1[NV], t2[NV];
-  load_tile<DT, VEC, NV>(tile_of(0), nu, t0);
-  if (1 < nrows) load_tile<DT, VEC, NV>(tile_of(1), nu, t1);
-  if (2 < nrows) load_tile<DT, VEC, NV>(tile_of(2), nu, t2);
-  // The draft tokens (and, from slice 0, the slot records of the target rows) go out with the
-  // first rows' loads.
-  if (tid < gb) {
-    const int32_t x = P.tokens[dbase + tid];
-    s_tok[tid] = x;
-    if (split == 0) {
-      SlotRec *rec = P.rec + slot0 + tid;
-      put_u32<true>(&rec->tok, (uint32_t)x);
-      put_u32<true>(&rec->u, __float_as_uint(sampling ? P.uniforms[2 * (dbase + b + tid)] : 0.f));
-    }
+  // live row r of the request: target rows 0..gb (slot r), then draft rows (slot gamma+1+i)
+  int32_t r;
+  const void *base;
+  int64_t row;
+  int32_t pos;
+  if (k <= P.gamma) {
+    if (k > gb) return;
+    r = k;
+    base = P.target;
+    row = dbase + b + k;
+    pos = k;
+  } else {
+    const int32_t i = k - P.gamma - 1;
+    if (i >= gb || !sampling) return;
+    r = gb + 1 + i;
+    base = P.draft;
+    row = dbase + i;
+    pos = i;
   }
-  __syncthreads();
-  // Statistics of loop row r from its tile, then the tile is refilled with row r + 3.
-  auto row_stats = [&](int32_t r, typename U::Raw(&t)[NV]) __attribute__((always_inline)) {
-    const bool tgt = r <= gb;
-    const int32_t pos = tgt ? r : r - gb - 1;
-    const int32_t k = tgt ? r : P.gamma + 1 + pos;
-    const int32_t tok = sampling && pos < gb ? s_tok[pos] : -1;
-    tile_stats<DT, VEC, NV, true>(t, tile_of(r), nu, lo, hi, T, tok,
-                                  P.parts + (slot0 + k) * P.nsplit + split, &P.rec[slot0 + k].z,
-                                  sh);
-    if (r + 3 < nrows) load_tile<DT, VEC, NV>(tile_of(r + 3), nu, t);
-  };
-  for (int32_t r = 0; r < nrows; r += 3) {  // uniform across the workgroup
-    row_stats(r, t0);
-    if (r + 1 < nrows) row_stats(r + 1, t1);
-    if (r + 2 < nrows) row_stats(r + 2, t2);
+  const int64_t lo = (int64_t)blockIdx.x * P.split_len;
+  const int64_t hi = lo + P.split_len < P.V ? lo + P.split_len : P.V;
+  const Store *tile = static_cast<const Store *>(row_ptr<DT>(base, row, P.V)) + lo / W;
+  const int32_t nu = (int32_t)((hi - lo + W - 1) / W);
+  {
+    // the tile's loads go out first: the token and its record wait on their own round trip
+    typename U::Raw raw[NV];
+    load_tile<DT, VEC, NV>(tile, nu, raw);
+    const int32_t xtok = pos < gb ? P.tokens[dbase + pos] : -1;
+    if (k <= P.gamma && pos < gb && blockIdx.x == 0 && tid == 0) {
+      put_u32<true>(&P.rec[slot].tok, (uint32_t)xtok);
+      put_u32<true>(&P.rec[slot].u,
+                    __float_as_uint(sampling ? P.uniforms[2 * (dbase + b + pos)] : 0.f));
+    }
+    tile_stats<DT, VEC, NV, true>(raw, tile, nu, lo, hi, T, sampling ? xtok : -1,
+                                  P.parts + (int64_t)slot * P.nsplit + blockIdx.x,
+                                  &P.rec[slot].z, sh);
   }
 
   // Arrival: this workgroup's stores are complete before it counts itself in.
+  const int32_t nrows = gb + 1 + (sampling ? gb : 0);
+  const uint32_t n = (uint32_t)nrows * (uint32_t)P.nsplit;  // the request's tiles
+  const int32_t w = r * P.nsplit + (int32_t)blockIdx.x;        // this tile among them
   wait_memory();
   __syncthreads();
-  const uint32_t n = (uint32_t)P.nsplit;
+  uint32_t *arrive = &P.arrive[b * kCounterStride];
   if (tid == 0) {
     const uint32_t old =
-        __hip_atomic_fetch_add(&P.arrive[b * kCounterStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int32_t go = old == n - 1u ? 2 : 1;  // 2: the last arrival
     if (go == 1 && sampling) {
       uint32_t spins = 0;
-      while (__hip_atomic_load(&P.arrive[b * kCounterStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n) {
+      while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n) {
         __builtin_amdgcn_s_sleep(1);
         if (++spins == kSpinLimit) {
           go = -1;
@@ -1350,28 +1340,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     return;
   }
   if (!sampling && tid == 0)
-    __hip_atomic_store(&P.arrive[b * kCounterStride], 0u, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   int64_t db;
   int32_t g;
   bool smp;
-  const TempConst tc = finish_head<kThreads, true>(P, b, !sampling || split == 0, L, db, g, smp);
+  const TempConst tc = finish_head<kThreads, true>(P, b, !sampling || w == 0, L, db, g, smp);
   if (!sampling) return;
   const Stop st = make_stop(L, gb, P.gamma + 1, tc, dbase + b + L.j, dbase + L.j);
-  // This slice of the stop row(s): lo is a multiple of kOneAlign elements, so its first unit
-  // starts a 64-unit chunk.
+  // This tile's share of the stop row(s): whole 64-unit chunks, spread over the request's n
+  // tiles (some shares may be empty).
+  const int64_t nunits = (P.V + W - 1) / W;
+  const int64_t su = ceil_div_dev(ceil_div_dev(nunits, (int64_t)n), kChunkUnits) * kChunkUnits;
+  const int64_t ub = (int64_t)w * su;
+  const int64_t ue = ub + su < nunits ? ub + su : nunits;
   double *cs = P.chunk_sums + (int64_t)b * P.chunk_stride;
-  stream_chunks<DT, VEC, kThreads, kFinRU>(P, st, lo / W, lo / W + nu, cs);
+  if (ub < ue) stream_chunks<DT, VEC, kThreads, kFinRU>(P, st, ub, ue, cs);
   wait_memory();
   __syncthreads();
+  uint32_t *odone = &P.odone[b * kCounterStride];
   if (tid == 0)
-    s_go = __hip_atomic_fetch_add(&P.odone[b * kCounterStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+    s_go = __hip_atomic_fetch_add(odone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
            n - 1u;
   __syncthreads();
   if (!s_go) return;
   if (tid == 0) {
-    __hip_atomic_store(&P.arrive[b * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&P.odone[b * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(odone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   draw_token<DT, VEC, kThreads>(P, b, st, cs, D);
 }
@@ -1589,8 +1583,6 @@ __global__ __launch_bounds__(kNgramPackThreads) void k_ngram_pack(NgramParams G)
 struct Plan {
   int32_t spr, nsplit;       // row slots per request; k_rowstats tiles per row
   int64_t split_len, chunk_stride;
-  int32_t one_nsplit;        // k_onepass workgroups per request; 0: the call cannot take it
-  int64_t one_split_len;
   size_t off_sync, off_parts, off_rec, off_chunks, off_done, total;
 };
 
@@ -1616,27 +1608,14 @@ bool make_plan(int32_t B, int32_t gamma, int64_t V, int dtype, bool greedy, Plan
   }
   pl.nsplit = (int32_t)ceil_div(V, len);  // no empty slice
   pl.split_len = len;
-  // k_onepass: slices of whole kOneAlign blocks, at most kOneTileBytes of a row; when requests
-  // are few, enough slices for about kOneTargetWgs workgroups; at most kOneMaxSlices.
-  {
-    const int64_t least = ceil_div(V, kOneTileBytes / (dtype == SPEC_F32 ? 4 : 2));
-    int64_t want = ceil_div(kOneTargetWgs, bb);
-    const int64_t cap = ceil_div(V, kOneAlign);
-    if (want > cap) want = cap;
-    if (want > kOneMaxSlices) want = kOneMaxSlices;
-    if (want < least) want = least;
-    pl.one_split_len = ceil_div(ceil_div(V, want), kOneAlign) * kOneAlign;
-    const int64_t ns = ceil_div(V, pl.one_split_len);
-    pl.one_nsplit = ns <= kOneMaxSlices && bb <= kOneMaxB ? (int32_t)ns : 0;
-  }
-  const int64_t parts_split = pl.nsplit > pl.one_nsplit ? pl.nsplit : pl.one_nsplit;
+  // (k_onepass uses whole kTileElems tiles: never more per row than k_rowstats)
   // Chunk sums of the stop rows; the element path (one element per unit) has the most chunks.
   pl.chunk_stride = ceil_div(V, kChunkUnits);
   // The one-launch counters sit first, at the same place and size for every call, so that
   // calls of any shape find them as the last call left them: zero.
   pl.off_sync = 0;
   pl.off_parts = align_up(2 * (size_t)kOneMaxB * kCounterStride * sizeof(uint32_t));
-  pl.off_rec = pl.off_parts + align_up((size_t)bb * pl.spr * parts_split * sizeof(Partial));
+  pl.off_rec = pl.off_parts + align_up((size_t)bb * pl.spr * pl.nsplit * sizeof(Partial));
   pl.off_chunks = pl.off_rec + align_up((size_t)bb * pl.spr * sizeof(SlotRec));
   pl.off_done = pl.off_chunks +
                 (greedy ? 0 : align_up((size_t)bb * pl.chunk_stride * sizeof(double)));
@@ -1680,56 +1659,39 @@ int resident_capacity(const void *kernel) {
   return per * cus;
 }
 
-// The library's own choice of one launch, where it measured faster on MI355X:
-//  - greedy calls of at most kOneGreedyTiles row tiles (one resident wave of k_greedy1);
-//  - sampling calls with at most one draft per request (three rows) and at most
-//    kOneSingleDraftGrid k_onepass workgroups.
-// Elsewhere two launches measured faster or equal (the one-launch workgroup reduces its rows
-// one after another).  Rows that are not 16-byte aligned take two launches too (the
-// one-launch kernel's element-path variant spills registers).
-constexpr int64_t kOneGreedyTiles = 2048;
-constexpr int64_t kOneSingleDraftGrid = 512;
+// The library's own choice of one launch, where it measured faster on MI355X: calls of at most
+// kOneAutoTiles row tiles with 16-byte aligned rows (and, with sampled requests, within three
+// quarters of the device's resident capacity).  Larger calls measured faster or equal in two
+// launches (greedy: 4608 tiles equal, 41472 tiles 25% slower in one).
+constexpr int64_t kOneAutoTiles = 2048;
 
 template <int DT, bool VEC>
 int run(Params P, const Plan &pl, const spec_probe *probe, hipStream_t s) {
   const int asked = probe ? probe->path : SPEC_PATH_AUTO;
   if (asked != SPEC_PATH_AUTO && asked != SPEC_PATH_TWO && asked != SPEC_PATH_ONE)
     return SPEC_ERR_SHAPE;
-  const int64_t tiles = (int64_t)P.B * pl.spr * ceil_div(P.V, kTileElems);
-  int path = asked;
-  if (path == SPEC_PATH_AUTO) {
-    const bool one = P.B <= kOneMaxB &&
-                     (P.greedy_all ? tiles <= kOneGreedyTiles
-                                   : VEC && P.gamma <= 1 && pl.one_nsplit > 0 &&
-                                         (int64_t)P.B * pl.one_nsplit <= kOneSingleDraftGrid);
-    path = one ? SPEC_PATH_ONE : SPEC_PATH_TWO;
-  }
-  if (path == SPEC_PATH_ONE && P.greedy_all) {
-    // greedy: row-statistics tiles whose last arrival per request finishes it
-    if (P.B > kOneMaxB) return SPEC_ERR_SHAPE;
-    const int64_t slots = (int64_t)P.B * pl.spr;
-    const uint32_t gy = (uint32_t)(slots < kMaxGridY ? slots : kMaxGridY);
-    const uint32_t gz = (uint32_t)ceil_div(slots, gy);
-    P.split_len = kTileElems;
-    P.nsplit = (int32_t)ceil_div(P.V, kTileElems);
-    return launch(k_greedy1<DT, VEC>, dim3((uint32_t)P.nsplit, gy, gz), kRsThreads, probe, 0, s,
-                  P);
-  }
-  if (path == SPEC_PATH_ONE) {
-    // every polling workgroup needs its siblings resident: keep a quarter of the device's
-    // capacity for this kernel spare
-    const int64_t grid = (int64_t)P.B * pl.one_nsplit;
-    const int64_t cap = resident_capacity(reinterpret_cast<const void *>(k_onepass<DT, VEC>));
-    if (pl.one_nsplit > 0 && grid <= cap * 3 / 4) {
-      P.nsplit = pl.one_nsplit;
-      P.split_len = pl.one_split_len;
-      return launch(k_onepass<DT, VEC>, dim3((uint32_t)grid), kThreads, probe, 0, s, P);
-    }
-    if (asked == SPEC_PATH_ONE) return SPEC_ERR_SHAPE;
-  }
   const int64_t slots = (int64_t)P.B * pl.spr;
   const uint32_t gy = (uint32_t)(slots < kMaxGridY ? slots : kMaxGridY);
   const uint32_t gz = (uint32_t)ceil_div(slots, gy);
+  if (asked != SPEC_PATH_TWO && P.B <= kOneMaxB) {
+    // one launch: whole kTileElems tiles; a call with sampled requests also needs all of its
+    // workgroups resident at once (three quarters of the device's capacity, to spare)
+    const int64_t ns = ceil_div(P.V, kTileElems);
+    const int64_t tiles = slots * ns;
+    bool one = asked == SPEC_PATH_ONE || (VEC && tiles <= kOneAutoTiles);
+    if (one && !P.greedy_all)
+      one = tiles * 4 <= 3 * (int64_t)resident_capacity(
+                                 reinterpret_cast<const void *>(k_onepass<DT, VEC>));
+    if (one) {
+      P.nsplit = (int32_t)ns;
+      P.split_len = kTileElems;
+      const dim3 grid((uint32_t)ns, gy, gz);
+      // greedy calls: k_greedy1, whose greedy-only code measured faster than k_onepass's
+      return P.greedy_all ? launch(k_greedy1<DT, VEC>, grid, kRsThreads, probe, 0, s, P)
+                          : launch(k_onepass<DT, VEC>, grid, kRsThreads, probe, 0, s, P);
+    }
+  }
+  if (asked == SPEC_PATH_ONE) return SPEC_ERR_SHAPE;
   // k_finish: enough slices of the stop rows per request for about kFinGrid workgroups, each
   // at least one pass and a whole number of 64-unit chunks.  Greedy calls need slice 0 only.
   const int64_t nunits = ceil_div(P.V, Unit<DT, VEC>::W);
