@@ -74,15 +74,24 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
+def kernel_source_digest() -> str:
+    """sha256 of the kernel source's code: comments and whitespace removed, so that only a
+    change of the code itself voids the committed counter runs."""
+    import re
+    text = KERNEL_SRC.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return hashlib.sha256(re.sub(r"\s+", "", text).encode()).hexdigest()
+
+
 def traffic_for_current_kernel(kernel: str, workload: int):
     """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter runs for this
-    workload, or None if there are none or the kernel source changed since they were taken."""
+    workload, or None if there are none or the kernel code changed since they were taken."""
     path = PROFILES / f"{kernel}_workload{workload}_traffic.json"
     if not path.exists():
         return None
     rec = json.loads(path.read_text())
-    sha = hashlib.sha256(KERNEL_SRC.read_bytes()).hexdigest()
-    if rec.get("source_sha256") != sha:
+    if rec.get("code_sha256") != kernel_source_digest():
         return None
     return rec
 

@@ -426,7 +426,8 @@ template <int NW>
 __device__ int32_t block_first(bool pred, int32_t *sh) {
   const uint64_t m = __ballot(pred);
   if ((threadIdx.x & 63) == 0)
-    sh[threadIdx.x >> 6] = m ? (int32_t)(threadIdx.x & ~63u) + __ffsll((long long)m) - 1 : INT32_MAX;
+    sh[threadIdx.x >> 6] =
+        m ? (int32_t)(threadIdx.x & ~63u) + __ffsll((long long)m) - 1 : INT32_MAX;
   __syncthreads();
   int32_t r = INT32_MAX;
 #pragma unroll
@@ -593,7 +594,8 @@ __device__ __forceinline__ void tile_stats(const typename Unit<DT, VEC>::Raw (&r
       }
       const double S = block_sum1<NW>((double)us[0], sh.sum);
       // to the shifted form, sum 2^((z - M) c): factor 2^(K - M c), one rounding
-      if (tid == 0) put_partial<SHARED>(out, Partial{M, 0, S * exp2(fma(-(double)M, tc.c, (double)K))});
+      if (tid == 0)
+        put_partial<SHARED>(out, Partial{M, 0, S * exp2(fma(-(double)M, tc.c, (double)K))});
     } else {
       // Extreme temperatures or logits: overflow-safe arguments, units re-read one at a time
       // (cache hits) to keep this rare path out of the common path's registers.
@@ -817,7 +819,8 @@ __device__ __forceinline__ TempConst finish_head(const Params &P, int32_t b, boo
     pv[q].m = -INFINITY;
     pv[q].idx = INT32_MAX;
     pv[q].s = 0.0;
-    if (k < P.spr && sl < P.nsplit) pv[q] = get_partial<SHARED>(P.parts + (slot0 + k) * P.nsplit + sl);
+    if (k < P.spr && sl < P.nsplit)
+      pv[q] = get_partial<SHARED>(P.parts + (slot0 + k) * P.nsplit + sl);
   }
   sampling = T > 0.f;
   const int64_t tbase = dbase + b;
@@ -848,7 +851,8 @@ __device__ __forceinline__ TempConst finish_head(const Params &P, int32_t b, boo
       if (sampling) {
         float m = live ? pv[q].m : -INFINITY;
         if (live)
-          for (int32_t p = sl + lp; p < P.nsplit; p += lp) m = fmaxf(m, get_partial<SHARED>(rowp + p).m);
+          for (int32_t p = sl + lp; p < P.nsplit; p += lp)
+            m = fmaxf(m, get_partial<SHARED>(rowp + p).m);
         for (int o = lp >> 1; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
         const float M = m;
         double f = 0.0;
@@ -1170,7 +1174,8 @@ __global__ __launch_bounds__(kThreads) void k_finish(Params P) {
   wait_memory();
   __syncthreads();
   if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(&P.done[b * kCounterStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+    s_last = __hip_atomic_fetch_add(&P.done[b * kCounterStride], 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) ==
              (uint32_t)P.nslice - 1u;
   __syncthreads();
   if (!s_last) return;
@@ -1227,7 +1232,9 @@ __global__ __launch_bounds__(kRsThreads) void k_greedy1(Params P) {
                                     __HIP_MEMORY_SCOPE_AGENT) == n - 1u;
   __syncthreads();
   if (!s_last) return;
-  if (tid == 0) __hip_atomic_store(&P.arrive[b * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0)
+    __hip_atomic_store(&P.arrive[b * kCounterStride], 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   int64_t db;
   int32_t g;
   bool smp;
