@@ -87,8 +87,8 @@ enum {
  *                 device at once (at most three quarters of the device's capacity for the
  *                 kernel).  A request whose workgroups do not all arrive within a bounded wait
  *                 (seconds; only if other work keeps them from being resident) comes back with
- *                 out_num_accepted = -1, and the workspace must then be zero-filled again
- *                 before its next use.
+ *                 out_num_accepted = -1 (its token slots are then not valid), and the
+ *                 workspace must be zero-filled again before its next use.
  *  SPEC_PATH_AUTO the library's choice, the default: one launch for calls of at most 2048 row
  *                 tiles with 16-byte aligned rows that it can take, where it measured faster
  *                 on MI355X; two launches otherwise.
@@ -119,6 +119,9 @@ typedef struct spec_probe {
                          touched                                                        */
   int path;           /* SPEC_PATH_AUTO, _TWO or _ONE; _ONE on a call that cannot take it,
                          or another value, returns SPEC_ERR_SHAPE                         */
+  unsigned int spin_limit; /* polls after which a bounded wait of the one-launch path gives
+                         up (0: the library's default, 2^22); a small value makes the
+                         time-out handling run, for tests of it                         */
 } spec_probe;
 
 /*

@@ -37,7 +37,7 @@ class _Probe(ctypes.Structure):
                 ("row_max_t", ctypes.c_void_p), ("row_sum_t", ctypes.c_void_p),
                 ("row_max_d", ctypes.c_void_p), ("row_sum_d", ctypes.c_void_p),
                 ("resid_mass", ctypes.c_void_p), ("events", ctypes.c_void_p * 8),
-                ("path", ctypes.c_int)]
+                ("path", ctypes.c_int), ("spin_limit", ctypes.c_uint)]
 
 
 def lib():
@@ -114,9 +114,11 @@ def _stream(stream):
 
 
 def make_probe(p_x=None, q_x=None, row_max_t=None, row_sum_t=None, row_max_d=None,
-               row_sum_d=None, resid_mass=None, events=None, path=SPEC_PATH_AUTO) -> _Probe:
+               row_sum_d=None, resid_mass=None, events=None, path=SPEC_PATH_AUTO,
+               spin_limit=0) -> _Probe:
     """Diagnostics and launch-control struct; tensors (device) or None, ``events`` a list of
-    up to 8 raw hipEvent_t handles (ints) or None, ``path`` one of SPEC_PATH_*."""
+    up to 8 raw hipEvent_t handles (ints) or None, ``path`` one of SPEC_PATH_*,
+    ``spin_limit`` the one-launch path's polling bound (0: the library's default)."""
     pr = _Probe()
     torch = _torch()
     for name, t, dt in (("p_x", p_x, torch.float64), ("q_x", q_x, torch.float64),
@@ -130,6 +132,7 @@ def make_probe(p_x=None, q_x=None, row_max_t=None, row_sum_t=None, row_max_d=Non
     for i, e in enumerate(events or []):
         pr.events[i] = e
     pr.path = int(path)
+    pr.spin_limit = int(spin_limit)
     return pr
 
 

@@ -78,7 +78,8 @@ constexpr int kChunkUnits = 64;              // residual sums: one per 64 units 
 constexpr int kOneMaxB = 2048;               // requests the one-launch counters cover
 constexpr int kCounterStride = 32;           // one counter per 128-byte line: atomics on a line
                                              // serialise, so requests must not share one
-constexpr uint32_t kSpinLimit = 1u << 22;    // polls before a one-launch workgroup stops waiting
+constexpr uint32_t kSpinLimit = 1u << 22;    // default polls before a one-launch workgroup
+                                             // stops waiting
 constexpr int64_t kMaxV = int64_t(1) << 24;
 constexpr double kLog2e = 1.4426950408889634074;
 constexpr size_t kAlign = 256;
@@ -139,6 +140,7 @@ struct Params {
   int32_t nsplit;           // k_rowstats tiles (slices) per row
   int64_t split_len;        // elements per slice: one tile, or less for small problems
   int32_t greedy_all;
+  uint32_t spin_limit;      // polls before a one-launch workgroup stops waiting
   double *p_x, *q_x, *row_sum_t, *row_sum_d, *resid_mass;
   float *row_max_t, *row_max_d;
 };
@@ -780,12 +782,15 @@ struct ReqLds {
 //  2. accept tests lane-parallel on wavefront 0 (p(x), q(x) in fp64 from the logits that
 //     k_rowstats captured) and the first rejection by ballot + find-first-set.
 // Merged rows sit in L by row slot (target row r at r, draft row i at gamma + 1 + i).  With
-// `write`, the outputs and the row probes are written.  Ends with a barrier; the stop row is
+// `write`, the outputs and the row probes are written (out_num_accepted only with `write_n`:
+// the one-launch path leaves a sampled request's count to the workgroup that draws, so that a
+// timed-out request keeps -1).  Ends with a barrier; the stop row is
 // in L.j.  Returns the request's temperature constant.  SHARED: the partials and slot records
 // were written by other workgroups of the same launch.
 template <int NT, bool SHARED>
 __device__ __forceinline__ TempConst finish_head(const Params &P, int32_t b, bool write, ReqLds &L,
-                                 int64_t &dbase, int32_t &gb, bool &sampling) {
+                                 int64_t &dbase, int32_t &gb, bool &sampling,
+                                 bool write_n = true) {
   constexpr int NW = NT / 64;
   constexpr int G = 4;  // rounds of row slots whose partials are loaded at once
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -915,7 +920,7 @@ __device__ __forceinline__ TempConst finish_head(const Params &P, int32_t b, boo
       if (lane == 0) {
         if (j < gb) P.out_tokens[tbase + gb] = -1;
         if (!sampling) P.out_tokens[tbase + j] = L.i[j];
-        P.out_n[b] = j;
+        if (write_n) P.out_n[b] = j;
       }
       if (sampling && lane < gb) {
         if (P.p_x) P.p_x[dbase + lane] = p;
@@ -1255,7 +1260,8 @@ __global__ __launch_bounds__(kRsThreads) void k_greedy1(Params P) {
 //    sums, and adds itself to a second counter; the last one draws, as in k_finish.
 // The last user of each counter returns it to zero.  A request whose workgroups do not all
 // arrive within the bound (only possible if they could not all be resident) is reported with
-// out_num_accepted = -1.
+// out_num_accepted = -1: a workgroup that gives up writes it, and a sampled request's count is
+// written only by the workgroup that draws, which a request with a time-out never reaches.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kRsThreads) void k_onepass(Params P) {
   using U = Unit<DT, VEC>;
@@ -1331,7 +1337,7 @@ __global__ __launch_bounds__(kRsThreads) void k_onepass(Params P) {
       uint32_t spins = 0;
       while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n) {
         __builtin_amdgcn_s_sleep(1);
-        if (++spins == kSpinLimit) {
+        if (++spins == P.spin_limit) {
           go = -1;
           break;
         }
@@ -1351,7 +1357,8 @@ __global__ __launch_bounds__(kRsThreads) void k_onepass(Params P) {
   int64_t db;
   int32_t g;
   bool smp;
-  const TempConst tc = finish_head<kThreads, true>(P, b, !sampling || w == 0, L, db, g, smp);
+  const TempConst tc =
+      finish_head<kThreads, true>(P, b, !sampling || w == 0, L, db, g, smp, !sampling);
   if (!sampling) return;
   const Stop st = make_stop(L, gb, P.gamma + 1, tc, dbase + b + L.j, dbase + L.j);
   // This tile's share of the stop row(s): whole 64-unit chunks, spread over the request's n
@@ -1373,6 +1380,9 @@ __global__ __launch_bounds__(kRsThreads) void k_onepass(Params P) {
   if (tid == 0) {
     __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(odone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Only a request all of whose workgroups finished gets its count; after a time-out
+    // nothing draws and the -1 stays.
+    P.out_n[b] = L.j;
   }
   draw_token<DT, VEC, kThreads>(P, b, st, cs, D);
 }
@@ -1675,6 +1685,7 @@ constexpr int64_t kOneAutoTiles = 2048;
 template <int DT, bool VEC>
 int run(Params P, const Plan &pl, const spec_probe *probe, hipStream_t s) {
   const int asked = probe ? probe->path : SPEC_PATH_AUTO;
+  P.spin_limit = probe && probe->spin_limit ? probe->spin_limit : kSpinLimit;
   if (asked != SPEC_PATH_AUTO && asked != SPEC_PATH_TWO && asked != SPEC_PATH_ONE)
     return SPEC_ERR_SHAPE;
   const int64_t slots = (int64_t)P.B * pl.spr;

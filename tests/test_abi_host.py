@@ -156,3 +156,21 @@ def test_workspace_keeps_a_fixed_counter_region():
     # so sizes grow by that much at least and any shape finds them at offset 0
     assert sv.spec_verify_workspace_size(1, 0, 1, sv.SPEC_F32) >= sv.COUNTER_BYTES
     assert sv.spec_verify_workspace_size(1, 0, 1, sv.SPEC_F32) < sv.COUNTER_BYTES + 4096
+
+
+def test_probe_struct_matches_the_header(tmp_path):
+    # the binding's ctypes mirror of spec_probe against the C compiler's layout of the header
+    import subprocess
+    fields = [f for f, _ in sv._Probe._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include "spec_verify.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(spec_probe));\n' +
+                   "".join(f'  printf("%zu\\n", offsetof(spec_probe, {f}));\n' for f in fields) +
+                   "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", str(ROOT / "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(sv._Probe)
+    assert got[1:] == [getattr(sv._Probe, f).offset for f in fields]

@@ -148,6 +148,38 @@ def test_one_launch_refuses_calls_it_cannot_take():
     assert launches(w) == 2     # the library's own choice takes two
 
 
+def test_one_launch_time_out_reports_minus_one_and_recovers():
+    # The one-launch path's bounded wait, forced from the host: with a polling bound of one, a
+    # workgroup that finds its request's tiles not all in gives up at once.  Each sampled
+    # request then comes back with out_num_accepted = -1 or complete and right (greedy
+    # requests never wait); after the counters are zeroed again the next call is whole.
+    import torch
+    B, gamma, V = 16, 4, 65536
+    temps = np.where(np.arange(B) % 4 == 1, 0.0, 0.8)
+    w = workloads.small(B=B, gamma=gamma, V=V, dtype="bf16", seed=77, temperatures=temps,
+                        draft_sigma=0.9)
+    print(f"[gpu] one-launch time-out B={B} gamma={gamma} V={V}", flush=True)
+    d = to_device(w)
+    ws = sv.alloc_workspace(B, gamma, V, sv.SPEC_BF16)
+    o = oracle.verify(w)
+    for spin in (1, 0):
+        out = torch.full((w.R_t,), -7, dtype=torch.int32, device="cuda")
+        nacc = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+        sv.spec_verify_sample(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temps"],
+                              gamma, out, nacc, ws, probe=sv.make_probe(path=ONE, spin_limit=spin))
+        torch.cuda.synchronize()
+        g = dict(out_tokens=out.cpu().numpy(), num_accepted=nacc.cpu().numpy())
+        gave_up = g["num_accepted"] == -1
+        print(f"[gpu]   spin_limit={spin}: {int(gave_up.sum())} requests gave up", flush=True)
+        assert not gave_up[temps == 0].any()
+        if spin == 1:
+            assert gave_up.any()
+            ws[:sv.COUNTER_BYTES].zero_()  # what the header asks after a time-out
+        else:
+            assert not gave_up.any()
+        parity.compare(w, g, o, requests=np.flatnonzero(~gave_up), probes=False)
+
+
 @pytest.mark.parametrize("B", [8, 32])
 @PATHS
 def test_single_draft_small_batch(B, path):
