@@ -72,13 +72,21 @@ def test_greedy_rejects_null_pointers(field):
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=2), -3), (dict(dtype=-1), -3),
     (dict(B=-1), -2), (dict(gamma=-1), -2), (dict(gamma=65), -2), (dict(V=0), -2),
-    (dict(V=1 << 31), -2),
+    (dict(V=1 << 31), -2), (dict(V=(1 << 24) + 1), -2),
     (dict(wsb=16), -4), (dict(ws=P(4096 + 8)), -4),
 ])
 def test_bad_arguments_return_codes(kw, code):
     assert _sample(**kw) == code
     kw = {k: v for k, v in kw.items()}
     assert _greedy(**kw) == code
+
+
+def test_largest_vocabulary_is_accepted():
+    # V = 2^24 is the largest vocabulary; its workspace is sized, and only the workspace
+    # (too small here) stops the call before anything is enqueued
+    assert sv.spec_verify_workspace_size(2, 2, 1 << 24, sv.SPEC_BF16) > 0
+    assert _sample(V=1 << 24, wsb=4096) == -4
+    assert _greedy(V=1 << 24, wsb=4096) == -4
 
 
 def test_empty_batch_is_a_no_op():

@@ -285,6 +285,15 @@ def test_gamma_zero_and_max_gamma(path):
     assert (o["num_accepted"] == 64).all()   # drafts are the target argmax: all accepted
 
 
+def test_largest_vocabulary():
+    # V = 2^24, the largest the library takes: 1024 tiles per row, chunk sums over 2^21
+    # units, the draw's scan over 32768 chunks; sampled and greedy requests
+    w = workloads.small(B=2, gamma=2, V=1 << 24, dtype="bf16", seed=24,
+                        temperatures=np.array([0.8, 0.0]), target_sigma=3.0, draft_sigma=0.5)
+    _both(w)
+    _both(w, greedy=True)
+
+
 @PATHS
 def test_ragged_with_empty_requests(path):
     base = workloads.small(B=6, gamma=5, V=777, dtype="bf16", seed=4, ragged=True,
