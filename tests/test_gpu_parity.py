@@ -294,6 +294,15 @@ def test_largest_vocabulary():
     _both(w, greedy=True)
 
 
+def test_requests_beyond_one_grid_dimension():
+    # 70000 requests: more row slots (210000) than one grid dimension holds, and more requests
+    # than the finishing launch's y dimension, so the z dimension carries the rest in both
+    w = workloads.small(B=70000, gamma=1, V=40, dtype="f32", seed=70, draft_sigma=0.8,
+                        temperatures=np.where(np.arange(70000) % 3 == 0, 0.0, 0.9))
+    _both(w)
+    _both(w, greedy=True)
+
+
 @PATHS
 def test_ragged_with_empty_requests(path):
     base = workloads.small(B=6, gamma=5, V=777, dtype="bf16", seed=4, ragged=True,
