@@ -294,6 +294,26 @@ def test_largest_vocabulary():
     _both(w, greedy=True)
 
 
+@pytest.mark.parametrize("sigma,V,dtype,resid_abs", [
+    (0.02, 4096, "f32", None), (0.01, 32000, "bf16", None),
+    # q within ~0.1% of p: the residual mass at a rejection is ~1e-3, and the mass, a small
+    # difference of fp32-normalised probabilities, is held to its documented absolute bound
+    (0.003, 4096, "f32", 2e-7),
+])
+def test_nearly_equal_p_and_q(sigma, V, dtype, resid_abs):
+    # a draft that follows the target closely (high acceptance): the rare rejections stop at
+    # rows whose residual max(p - q, 0) is small and spread over half the vocabulary
+    w = workloads.small(B=3000, gamma=8, V=V, dtype=dtype, seed=int(sigma * 1000) + V,
+                        temperatures=1.0, target_sigma=2.0, draft_sigma=sigma)
+    g = run(w)
+    o = oracle.verify(w)
+    rej = o["num_accepted"] < w.gammas
+    assert rej.sum() >= 20
+    rep = parity.compare(w, g, o, resid_abs=resid_abs)
+    print(f"[gpu]   sigma {sigma}: {int(rej.sum())} rejections, residual mass there from "
+          f"{o['resid_mass'][rej].min():.2e}; {rep}", flush=True)
+
+
 def test_requests_beyond_one_grid_dimension():
     # 70000 requests: more row slots (210000) than one grid dimension holds, and more requests
     # than the finishing launch's y dimension, so the z dimension carries the rest in both
