@@ -1,4 +1,5 @@
-"""The entry points inside a captured HIP graph (torch.cuda.CUDAGraph).
+"""The entry points inside a captured HIP graph (torch.cuda.CUDAGraph), and on concurrent
+streams.
 
 The library neither allocates, synchronises nor records memset nodes during a call, so a
 serving loop can capture a whole step once and replay it.  Each test replays its graph
@@ -183,3 +184,46 @@ def test_decode_loop_replays_in_a_graph():
     np.testing.assert_array_equal(d["stats"].cpu().numpy().astype(np.uint64), stats_o)
     np.testing.assert_array_equal(d["hist"].cpu().numpy().astype(np.uint64), hist_o)
     assert accepted > steps * B  # the loop keeps drafting and accepting
+
+
+@pytest.mark.parametrize("path", [TWO, AUTO], ids=["two", "auto"])
+def test_concurrent_calls_on_two_streams(path):
+    # The library keeps no state between calls: two callers on two streams (default
+    # priority), each with its own workspace and outputs, interleave their calls; every result
+    # equals the same call made alone.  (The calls here are far below the one-launch path's
+    # resident bound, which AUTO takes for them, so both can be resident together.)
+    import torch
+    ws_list = [workloads.small(B=16, gamma=4, V=32000, dtype="bf16", seed=400 + i,
+                               ragged=i == 1, temperatures=np.where(np.arange(16) % 5 == 0,
+                                                                    0.0, 0.8))
+               for i in range(2)]
+    _say(f"two streams, path={path}")
+    dev = [workloads.to_torch(w) for w in ws_list]
+    wsp = [sv.alloc_workspace(w.B, w.gamma, w.V, sv.SPEC_BF16) for w in ws_list]
+    outs = [[torch.full((w.R_t,), -7, dtype=torch.int32, device="cuda") for _ in range(6)]
+            for w in ws_list]
+    naccs = [[torch.full((w.B,), -7, dtype=torch.int32, device="cuda") for _ in range(6)]
+             for w in ws_list]
+    probe = sv.make_probe(path=path)
+
+    def call(i, k):
+        w, d = ws_list[i], dev[i]
+        sv.spec_verify_sample(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temps"],
+                              w.gamma, outs[i][k], naccs[i][k], wsp[i], cu_draft=d["cu"],
+                              probe=probe)
+
+    for i in range(2):  # alone
+        call(i, 0)
+        torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for k in range(1, 6):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                call(i, k)
+    torch.cuda.synchronize()
+    for i in range(2):
+        for k in range(1, 6):
+            np.testing.assert_array_equal(outs[i][k].cpu().numpy(), outs[i][0].cpu().numpy())
+            np.testing.assert_array_equal(naccs[i][k].cpu().numpy(), naccs[i][0].cpu().numpy())
+        o = oracle.verify(ws_list[i])
+        assert (naccs[i][0].cpu().numpy() == o["num_accepted"]).mean() > 0.9
