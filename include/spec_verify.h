@@ -46,7 +46,8 @@
  * on the host before anything is enqueued, so an argument error leaves outputs untouched.
  * SPEC_ERR_HIP means a kernel launch failed; kernels of the same call launched before it
  * stay enqueued.  Device data are not checked (that would need a sync): logits must be
- * finite, cu_draft a valid CSR whose rows exist, uniforms in [0, 1).
+ * finite or -inf (a masked entry: probability 0) with at least one finite logit per row,
+ * cu_draft a valid CSR whose rows exist, uniforms in [0, 1).
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H

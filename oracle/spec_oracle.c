@@ -70,7 +70,8 @@ static void row_argmax(const void *base, int dtype, int64_t row, int64_t V,
   *idx_out = bi;
 }
 
-/* Softmax normaliser at temperature T: m = max_k z_k, S = sum_k exp((z_k - m) / T). */
+/* Softmax normaliser at temperature T: m = max_k z_k, S = sum_k exp((z_k - m) / T).  A masked
+ * logit (-inf) contributes exp(-inf) = 0; a row needs one finite logit. */
 static void row_softmax_stats(const void *base, int dtype, int64_t row, int64_t V, double T,
                               double *m_out, double *S_out) {
   double m;

@@ -168,10 +168,14 @@ struct TempConst {
   float c_hi, c_lo;
 };
 
+// c = log2(e)/T as c_hi + c_lo with c_lo > 0 strictly (c_hi is c rounded down, one ulp lower
+// where c is a float): a masked logit z = -inf then gives z c_hi + z c_lo = -inf and a term of
+// exactly 0, never -inf + inf or -inf * 0.
 __device__ __forceinline__ TempConst temp_const(float T) {
   double c = kLog2e / (double)T;
   if (c > 1e38) c = 1e38;  // temperatures below ~1.4e-38 act as ~1.4e-38
-  const float hi = (float)c;
+  float hi = (float)c;
+  if ((double)hi >= c) hi = __uint_as_float(__float_as_uint(hi) - 1u);  // hi > 0: one ulp down
   const float lo = (float)(c - (double)hi);
   return {(double)hi + (double)lo, hi, lo};
 }
@@ -571,7 +575,10 @@ __device__ __forceinline__ void tile_stats(const typename Unit<DT, VEC>::Raw (&r
     }
   }
 
-  if (T > 0.f) {
+  if (T > 0.f && M == -INFINITY) {
+    // every logit of the tile masked: no mass (the row has a finite logit elsewhere)
+    if (tid == 0) put_partial<SHARED>(out, Partial{M, 0, 0.0});
+  } else if (T > 0.f) {
     const TempConst tc = temp_const(T);
     if (fold_ok(M, tc.c_hi) && tc.c < 1e6 && tc.c > 1e-30) {
       // The common case: two-FMA exponent arguments.  In this range of c a filler's

@@ -314,6 +314,19 @@ def test_nearly_equal_p_and_q(sigma, V, dtype, resid_abs):
           f"{o['resid_mass'][rej].min():.2e}; {rep}", flush=True)
 
 
+@PATHS
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_masked_logits(path, dtype):
+    # Vocabulary masks (logit -inf, shared by a request's rows): 30% of the entries plus a run
+    # of 20000, so some 16K tiles are masked whole; temperatures across the range (the
+    # temperature constant's low part, kept positive, must not turn -inf into NaN)
+    temps = np.array([0.05, 0.3, 0.0, 0.7, 1.0, 1.3, 0.0, 2.5, 0.9, 0.6, 1.7, 0.45])
+    w = workloads.small(B=12, gamma=5, V=40000, dtype=dtype, seed=31, temperatures=temps,
+                        ragged=True, draft_sigma=0.8, mask_frac=0.3, mask_span=20000)
+    _both(w, path=path)
+    _both(w, greedy=True, path=path)
+
+
 def test_requests_beyond_one_grid_dimension():
     # 70000 requests: more row slots (210000) than one grid dimension holds, and more requests
     # than the finishing launch's y dimension, so the z dimension carries the rest in both

@@ -66,6 +66,40 @@ def test_row_statistics_and_probabilities_match_scipy_softmax(dtype, T):
             assert r["q_x"][db[b] + i] == pytest.approx(q_ref, rel=1e-12, abs=1e-300)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_masked_logits_have_zero_probability(dtype):
+    # Logits of -inf (a vocabulary mask, shared by a request's target and draft rows, with a
+    # long masked run) take probability 0: the statistics and p(x), q(x) are scipy's softmax
+    # over the same rows (which maps -inf to 0), no emitted token is a masked one, and greedy
+    # requests decode the argmax of the unmasked logits.
+    temps = np.array([0.7, 0.0, 1.3, 0.25, 1.0, 0.0])
+    w = workloads.small(B=6, gamma=4, V=3000, dtype=dtype, seed=13, temperatures=temps,
+                        ragged=True, mask_frac=0.4, mask_span=1200)
+    zt = workloads.decode(w.target, dtype)
+    zd = workloads.decode(w.draft, dtype)
+    assert np.isinf(zt).mean() > 0.5 and np.isinf(zd).any()
+    r = oracle.verify(w)
+    T32 = w.temperatures
+    tb_all, db_all = w.target_base, w.draft_base
+    for b, (tb, db, g) in enumerate(zip(tb_all, db_all, w.gammas)):
+        n = r["num_accepted"][b]
+        k = r["out_tokens"][tb + n]
+        assert np.isfinite(zt[tb + n, k])                   # never a masked token
+        if T32[b] > 0:
+            for i in range(g):
+                x = w.draft_tokens[db + i]
+                assert np.isfinite(zd[db + i, x])           # drawn from the masked q
+                p_ref = _softmax(zt[tb + i], T32[b])[x]
+                q_ref = _softmax(zd[db + i], T32[b])[x]
+                assert r["p_x"][db + i] == pytest.approx(p_ref, rel=1e-12, abs=1e-300)
+                assert r["q_x"][db + i] == pytest.approx(q_ref, rel=1e-12, abs=1e-300)
+            S_ref = np.exp(special.logsumexp((zt[tb] - zt[tb].max()) / T32[b]))
+            assert r["row_sum_t"][tb] == pytest.approx(S_ref, rel=1e-12)
+    out, nacc = _argmax_decoding(w)
+    greedy = T32 == 0
+    np.testing.assert_array_equal(r["num_accepted"][greedy], nacc[greedy])
+
+
 def _argmax_decoding(w):
     """Greedy verification written as target-argmax decoding with numpy.argmax
     (first occurrence of the maximum)."""

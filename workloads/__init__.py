@@ -143,8 +143,15 @@ def _gumbel_max(z: np.ndarray, T: float, rng: np.random.Generator) -> int:
 def generate(*, name: str, B: int, V: int, dtype: str, gammas: Sequence[int], dense: bool,
              target_sigma: float, draft_sigma, temperatures, seed: int,
              uniform_seed: Optional[int] = None, peaks: int = 0, peak_height: float = 8.0,
-             peak_rng_seed: Optional[int] = None, target_mean: float = 0.0) -> Workload:
+             peak_rng_seed: Optional[int] = None, target_mean: float = 0.0,
+             mask_frac: float = 0.0, mask_span: int = 0) -> Workload:
     """Generic seeded workload.
+
+    ``mask_frac`` / ``mask_span``: masked vocabulary entries (logit -inf), the same for every
+    row of a request, as a vocabulary constraint would set them: each entry with probability
+    ``mask_frac`` plus one run of ``mask_span`` consecutive entries, drawn per request from
+    the stream (``seed+6``, request); entry 0 stays unmasked if a mask would cover the row.
+    Draft rows inherit the mask (-inf plus noise), so draft tokens never land on it.
 
     Streams: logits ``seed+1``, draft noise ``seed+2``, peak indices ``peak_rng_seed``
     (default ``seed+3``), draft-token draws ``seed+4``, uniforms ``uniform_seed``
@@ -173,9 +180,24 @@ def generate(*, name: str, B: int, V: int, dtype: str, gammas: Sequence[int], de
 
     store_t = np.float32 if dtype == "f32" else np.uint16
     target = np.empty((R_t, V), dtype=store_t)
+    req_of_t = np.repeat(np.arange(B), gammas + 1)
+
+    def mask_of(b: int) -> np.ndarray:
+        mrng = np.random.default_rng([seed + 6, b])
+        m = mrng.random(V) < mask_frac
+        if mask_span:
+            start = int(mrng.integers(0, max(V - mask_span, 0) + 1))
+            m[start: start + mask_span] = True
+        if m.all():
+            m[0] = False
+        return m
+
     for r0 in range(0, R_t, _BLOCK):
         r1 = min(R_t, r0 + _BLOCK)
         blk = rng_logit.standard_normal((r1 - r0, V)) * target_sigma + target_mean
+        if mask_frac > 0 or mask_span > 0:
+            for r in range(r1 - r0):
+                blk[r, mask_of(int(req_of_t[r0 + r]))] = -np.inf
         if peaks:
             for r in range(r1 - r0):
                 idx = rng_peak.choice(V, size=peaks, replace=False)
@@ -311,9 +333,11 @@ def tiled(target_rows: np.ndarray, draft_rows: np.ndarray, n: int, *, T: float, 
 
 def small(*, B: int, gamma: int, V: int, dtype: str = "f32", seed: int = 0,
           temperatures=1.0, target_sigma: float = 2.0, draft_sigma=0.7,
-          ragged: bool = False, peaks: int = 0) -> Workload:
+          ragged: bool = False, peaks: int = 0, mask_frac: float = 0.0,
+          mask_span: int = 0) -> Workload:
     """Small seeded workload of the same construction, for tests.  ``ragged`` draws
-    gamma_b from U{1..gamma} and packs them as CSR offsets."""
+    gamma_b from U{1..gamma} and packs them as CSR offsets; ``mask_frac`` / ``mask_span`` as
+    for ``generate``."""
     prng = np.random.default_rng(seed + 3)
     if ragged:
         gam = prng.integers(1, gamma + 1, size=B)
@@ -322,7 +346,8 @@ def small(*, B: int, gamma: int, V: int, dtype: str = "f32", seed: int = 0,
     return generate(name=f"small B={B} gamma={gamma} V={V} {dtype}", B=B, V=V, dtype=dtype,
                     gammas=gam, dense=not ragged, target_sigma=target_sigma,
                     draft_sigma=draft_sigma, temperatures=temperatures, seed=seed,
-                    peaks=peaks, peak_rng_seed=seed + 6)
+                    peaks=peaks, peak_rng_seed=seed + 6, mask_frac=mask_frac,
+                    mask_span=mask_span)
 
 
 # ----------------------------------------------------------------------------- token contexts
