@@ -197,8 +197,9 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this step has no multi-GPU path (asked for "
-              f"--gpus {args.gpus}); per-request sharding across GPUs needs no communication "
-              f"and is described in DESIGN.md", file=sys.stderr)
+              f"--gpus {args.gpus}); requests are independent, so several GPUs would each run "
+              f"this step on their own share of the batch, with no communication",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
