@@ -203,16 +203,24 @@ def test_single_draft_decode_batch():
 
 def _random_case(i):
     """Seeded random call: B, gamma, V, dtype, dense or ragged, a mix of greedy and sampled
-    requests, target/draft closeness and temperatures over a wide range."""
+    requests, target/draft closeness and temperatures over a wide range; from case 24 on,
+    also vocabulary masks (-inf) and some extreme temperatures."""
     rng = np.random.default_rng(7000 + i)
     dtype = "bf16" if rng.random() < 0.6 else "f32"
     B = int(rng.integers(1, 48))
     gamma = int(rng.integers(1, 11))
     V = int(rng.choice([rng.integers(1, 600), rng.integers(600, 20000), rng.integers(20000, 130000)]))
     temps = np.where(rng.random(B) < 0.25, 0.0, rng.uniform(0.05, 2.0, B))
-    return dict(B=B, gamma=gamma, V=V, dtype=dtype, seed=7000 + i, ragged=bool(rng.random() < 0.6),
-                temperatures=temps, target_sigma=float(rng.uniform(0.5, 4.0)),
-                draft_sigma=float(rng.uniform(0.05, 1.5)))
+    kw = dict(B=B, gamma=gamma, V=V, dtype=dtype, seed=7000 + i, ragged=bool(rng.random() < 0.6),
+              temperatures=temps, target_sigma=float(rng.uniform(0.5, 4.0)),
+              draft_sigma=float(rng.uniform(0.05, 1.5)))
+    if i >= 24:
+        r2 = np.random.default_rng(9000 + i)
+        kw["mask_frac"] = float(r2.choice([0.0, 0.3, 0.7]))
+        kw["mask_span"] = int(r2.choice([0, V // 3, V // 2]))
+        extreme = r2.random(B)
+        kw["temperatures"] = np.where(extreme < 0.1, 1e-3, np.where(extreme > 0.9, 12.0, temps))
+    return kw
 
 
 def _one_launch_tiles(w, greedy=False):
@@ -226,7 +234,7 @@ def _one_launch_tiles(w, greedy=False):
 ONE_FITS = 900
 
 
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", range(48))
 def test_random_calls_on_both_paths(i):
     # the same seeded call on both launch paths (one launch where its workgroups fit): each
     # matches the oracle under the parity rules, and the two agree on every request the oracle
