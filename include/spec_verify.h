@@ -195,8 +195,9 @@ int spec_verify_greedy(const void *target_logits, int dtype, const int32_t *draf
  * to seq_tokens[b][seq_len[b] ..]; those at or past `capacity` are dropped and counted as
  * truncated; seq_len[b] becomes min(seq_len[b] + n_b + 1, capacity).  All pointers are device
  * pointers.  Errors: SPEC_ERR_SHAPE (B < 0, gamma outside [0, 64], capacity < 0), SPEC_ERR_NULL,
- * SPEC_ERR_HIP; B == 0 enqueues nothing.  Device data are not checked: n_b is clamped to
- * [0, gamma_b] and seq_len[b] to [0, capacity] for memory safety only.
+ * SPEC_ERR_HIP; B == 0 enqueues nothing.  A request whose n_b is -1 (the verification gave
+ * up on it) is left unchanged and not counted.  Device data are not checked: n_b is clamped
+ * to at most gamma_b and seq_len[b] to [0, capacity] for memory safety only.
  */
 int spec_verify_commit(const int32_t *out_tokens, const int32_t *out_num_accepted,
                        const int32_t *cu_draft, int32_t B, int32_t gamma, int32_t *seq_tokens,

@@ -1407,7 +1407,8 @@ struct CommitParams {
 
 // One thread per request: append the request's n_b + 1 emitted tokens to its history at
 // seq_len[b], clamp the length at capacity, and fold the step into the counters (wavefront
-// sums and an LDS histogram, then one device atomic per counter and bin per workgroup).
+// sums and an LDS histogram, then one device atomic per counter and bin per workgroup).  A
+// request whose count is negative (-1: its verification gave up) is left alone, uncounted.
 __global__ __launch_bounds__(kThreads) void k_commit(CommitParams C) {
   __shared__ unsigned long long s_sum[5][kWaves];
   __shared__ uint32_t s_hist[SPEC_MAX_GAMMA + 1];
@@ -1417,7 +1418,7 @@ __global__ __launch_bounds__(kThreads) void k_commit(CommitParams C) {
   __syncthreads();
   const int64_t b = (int64_t)blockIdx.x * kThreads + tid;
   unsigned long long v[5] = {0, 0, 0, 0, 0};
-  if (b < C.B) {
+  if (b < C.B && C.out_n[b] >= 0) {
     int64_t dbase, gb;
     if (C.cu) {
       dbase = C.cu[b];
@@ -1429,7 +1430,7 @@ __global__ __launch_bounds__(kThreads) void k_commit(CommitParams C) {
     // memory safety on device data the host cannot check
     gb = gb < 0 ? 0 : (gb > C.gamma ? C.gamma : gb);
     int64_t n = C.out_n[b];
-    n = n < 0 ? 0 : (n > gb ? gb : n);
+    n = n > gb ? gb : n;
     int64_t len = C.seq_len[b];
     len = len < 0 ? 0 : (len > C.capacity ? C.capacity : len);
     const int32_t *src = C.out_tokens + dbase + b;

@@ -534,10 +534,12 @@ def test_prepared_call_repeats_the_entry_point():
     np.testing.assert_array_equal(nacc.cpu().numpy(), refg["num_accepted"])
 
 
-@pytest.mark.parametrize("capacity,fill", [(64, "low"), (14, "high")])
-def test_commit_matches_oracle(capacity, fill):
+@pytest.mark.parametrize("capacity,fill,gave_up", [(64, "low", False), (14, "high", False),
+                                                   (64, "low", True)])
+def test_commit_matches_oracle(capacity, fill, gave_up):
     # the GPU commit of a verification step's outputs against the oracle's commit of the
-    # same outputs (histories and counters bit-exact)
+    # same outputs (histories and counters bit-exact); with gave_up, every seventh request
+    # carries the count -1 (a verification that gave up), which both leave alone
     import torch
     import speculative_sampling_verification_spec_amd as sv
     B, gamma = 300, 6
@@ -545,6 +547,8 @@ def test_commit_matches_oracle(capacity, fill):
     w = workloads.small(B=B, gamma=gamma, V=5000, dtype="bf16", seed=capacity, ragged=True,
                         temperatures=temps, draft_sigma=0.7)
     o = oracle.verify(w)   # both commits take the oracle's step as input
+    if gave_up:
+        o["num_accepted"][::7] = -1
     rng = np.random.default_rng(capacity)
     hi = capacity if fill == "high" else capacity - gamma - 1
     seq0 = rng.integers(0, 5000, size=(B, capacity)).astype(np.int32)
