@@ -140,7 +140,8 @@ typedef struct spec_probe {
  *  V              vocabulary size
  *  out_tokens     [R_t] int32      request b's slots 0..gamma_b: the n_b accepted drafts, the
  *                                  token emitted at the stop row n_b, then -1
- *  out_num_accepted [B] int32      n_b in [0, gamma_b]; the step emits n_b + 1 tokens
+ *  out_num_accepted [B] int32      n_b in [0, gamma_b]; the step emits n_b + 1 tokens (-1:
+ *                                  the one-launch path gave up on the request, see above)
  *  workspace      device scratch of at least spec_verify_workspace_size(B, gamma, V, dtype)
  *                 bytes, 256-byte aligned, zero-filled before its first use; every call
  *                 leaves it ready for the next, of any shape.  Its first 512 KiB hold the
