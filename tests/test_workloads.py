@@ -56,3 +56,22 @@ def test_gumbel_draft_draw_follows_the_tempered_softmax():
                                        np.random.default_rng(6))
     pval, _, _ = chi2_pvalue(np.bincount(toks, minlength=12), special.softmax(z / 0.6))
     assert pval > 1e-3
+
+
+def test_vocabulary_masks_are_shared_by_a_request_and_leave_a_finite_logit():
+    w = workloads.small(B=6, gamma=3, V=500, dtype="bf16", seed=4, ragged=True,
+                        temperatures=0.8, mask_frac=0.4, mask_span=200)
+    zt = workloads.decode(w.target, "bf16")
+    zd = workloads.decode(w.draft, "bf16")
+    for b, (tb, db, g) in enumerate(zip(w.target_base, w.draft_base, w.gammas)):
+        m = np.isinf(zt[tb])
+        assert 0.4 < m.mean() < 0.9 and not m.all()
+        for i in range(g + 1):
+            np.testing.assert_array_equal(np.isinf(zt[tb + i]), m)
+        for i in range(g):
+            np.testing.assert_array_equal(np.isinf(zd[db + i]), m)
+            assert not m[w.draft_tokens[db + i]]      # drafts are drawn from the masked q
+    # a mask that would cover a row keeps entry 0
+    w = workloads.small(B=2, gamma=1, V=50, dtype="f32", seed=5, mask_frac=1.0)
+    zt = workloads.decode(w.target, "f32")
+    assert np.isfinite(zt[:, 0]).all() and np.isinf(zt[:, 1:]).all()
