@@ -348,9 +348,30 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
 }
+// Lane moves within the wavefront by DPP (a VALU operand modifier, no LDS crossbar): CTRL
+// selects the source lane, ROWS the 16-lane rows that receive it (the others receive 0).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_move(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)b, CTRL, ROWS, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(b >> 32), CTRL, ROWS, 0xF, false);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) |
+                                          (unsigned long long)(unsigned)lo));
+}
+// Sum over the wavefront (every lane active), returned to every lane: pairs within quads, then
+// the half-row and row mirrors give each lane its 16-lane row's sum; the row broadcasts of
+// lane 15 (into rows 1 and 3) and lane 31 (into rows 2 and 3) leave the total in lane 63.
 __device__ __forceinline__ double wave_sum(double v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_move<0xB1, 0xF>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_move<0x4E, 0xF>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_move<0x141, 0xF>(v);  // row_half_mirror
+  v += dpp_move<0x140, 0xF>(v);  // row_mirror
+  v += dpp_move<0x142, 0xA>(v);  // row_bcast:15
+  v += dpp_move<0x143, 0xC>(v);  // row_bcast:31
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, 63);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), 63);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 __device__ __forceinline__ int32_t wave_min_i(int32_t v) {
   for (int o = 32; o > 0; o >>= 1) {
