@@ -344,10 +344,7 @@ __device__ __forceinline__ void wait_memory() {
 
 // ------------------------------------------------------------------ wave / block reductions
 
-__device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
+
 // Lane moves within the wavefront by DPP (a VALU operand modifier, no LDS crossbar): CTRL
 // selects the source lane, ROWS the 16-lane rows that receive it (the others receive 0).
 template <int CTRL, int ROWS>
@@ -373,12 +370,31 @@ __device__ __forceinline__ double wave_sum(double v) {
   const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), 63);
   return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
+
+// The same reduction pattern for 32-bit values; rows that do not receive a move get `id`,
+// the operation's identity.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_move32(int v, int id) {
+  return __builtin_amdgcn_update_dpp(id, v, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ float wave_max(float v) {
+  const int ninf = __float_as_int(-INFINITY);
+  v = fmaxf(v, __int_as_float(dpp_move32<0xB1, 0xF>(__float_as_int(v), ninf)));
+  v = fmaxf(v, __int_as_float(dpp_move32<0x4E, 0xF>(__float_as_int(v), ninf)));
+  v = fmaxf(v, __int_as_float(dpp_move32<0x141, 0xF>(__float_as_int(v), ninf)));
+  v = fmaxf(v, __int_as_float(dpp_move32<0x140, 0xF>(__float_as_int(v), ninf)));
+  v = fmaxf(v, __int_as_float(dpp_move32<0x142, 0xA>(__float_as_int(v), ninf)));
+  v = fmaxf(v, __int_as_float(dpp_move32<0x143, 0xC>(__float_as_int(v), ninf)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
 __device__ __forceinline__ int32_t wave_min_i(int32_t v) {
-  for (int o = 32; o > 0; o >>= 1) {
-    const int32_t t = __shfl_xor(v, o);
-    v = t < v ? t : v;
-  }
-  return v;
+  v = min(v, dpp_move32<0xB1, 0xF>(v, INT32_MAX));
+  v = min(v, dpp_move32<0x4E, 0xF>(v, INT32_MAX));
+  v = min(v, dpp_move32<0x141, 0xF>(v, INT32_MAX));
+  v = min(v, dpp_move32<0x140, 0xF>(v, INT32_MAX));
+  v = min(v, dpp_move32<0x142, 0xA>(v, INT32_MAX));
+  v = min(v, dpp_move32<0x143, 0xC>(v, INT32_MAX));
+  return __builtin_amdgcn_readlane(v, 63);
 }
 __device__ __forceinline__ void argmax_merge(float &bv, int32_t &bi, float ov, int32_t oi) {
   if (ov > bv || (ov == bv && oi < bi)) {
