@@ -403,12 +403,16 @@ __device__ __forceinline__ void argmax_merge(float &bv, int32_t &bi, float ov, i
   }
 }
 // Inclusive scan over a wavefront (fp64, lane order).
+// (by DPP: row shifts by 1, 2, 4 and 8 give each lane its prefix within its 16-lane row, lanes
+// shifted in from outside the row reading 0; the row broadcasts of lanes 15 and 31 then add
+// the rows before)
 __device__ __forceinline__ double wave_incl_scan(double v) {
-  const int lane = threadIdx.x & 63;
-  for (int o = 1; o < 64; o <<= 1) {
-    const double t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
+  v += dpp_move<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_move<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_move<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_move<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_move<0x142, 0xA>(v);  // row_bcast:15
+  v += dpp_move<0x143, 0xC>(v);  // row_bcast:31
   return v;
 }
 
