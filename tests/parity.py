@@ -11,7 +11,7 @@
   row maxima are bit-equal.  A caller may hold the residual mass of a rejection to an
   absolute bound instead (``resid_abs``): that mass is a difference of probabilities whose
   fp32 row sums carry ~1e-7 relative error, so its error is absolute (~1e-7) and exceeds
-  1e-5 relative once the mass falls below ~2e-3 (q within ~0.2% of p).
+  1e-5 relative once the mass falls to ~1e-2 or below (q within ~1% of p).
 * Invariants for every GPU request: 0 <= n <= gamma_b, the accepted prefix is the drafts,
   the stop slot holds an id in [0, V), the slots after it are -1.
 """
