@@ -193,6 +193,8 @@ def main():
     ap.add_argument("--single-draft", type=int, default=0, metavar="B",
                     help="instead of a workload: a decode batch of B requests with one draft "
                          "each (V = 128256 bf16, T = 0.7)")
+    ap.add_argument("--streams", type=int, default=1, metavar="S",
+                    help="also time independent batches spread over S streams (context figure)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -351,12 +353,51 @@ def main():
     result["context"] = context_figures()
     result["commit"] = time_commit(sv, w, out, nacc, d=inputs[0], steps=args.steps)
     result["ngram"] = time_ngram(sv, steps=args.steps)
+    if args.streams > 1:
+        result["independent_batches"] = time_streams(sv, w, inputs, code, path, all_greedy,
+                                                      args.streams, args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
 NGRAM = dict(B=512, capacity=8192, n_min=2, n_max=5, gamma=8, seed=77)
+
+
+def time_streams(sv, w, inputs, code, path, all_greedy, nstreams, steps):
+    """Calls over independent batches, round-robin over `nstreams` streams (default
+    priority), each call with its own workspace and outputs, so that one call's chain of
+    dependent steps can overlap another's logit stream.  A context figure for serving loops
+    that keep several batches in flight; the step time above is one call after another."""
+    import torch
+    streams = [torch.cuda.Stream() for _ in range(nstreams)]
+    ctl = sv.make_probe(path=path) if path else None
+    calls = []
+    for k in range(len(inputs) * nstreams):
+        d, s = inputs[k % len(inputs)], streams[k % nstreams]
+        ws = sv.alloc_workspace(w.B, w.gamma, w.V, code)
+        out = torch.empty(w.R_t, dtype=torch.int32, device="cuda")
+        nacc = torch.empty(w.B, dtype=torch.int32, device="cuda")
+        if all_greedy:
+            calls.append(sv.prepare_greedy(d["target"], d["tokens"], w.gamma, out, nacc, ws,
+                                           cu_draft=d["cu"], probe=ctl, stream=s))
+        else:
+            calls.append(sv.prepare_sample(d["target"], d["draft"], d["tokens"], d["uniforms"],
+                                           d["temps"], w.gamma, out, nacc, ws, cu_draft=d["cu"],
+                                           probe=ctl, stream=s))
+    torch.cuda.synchronize()
+    n = max(steps, len(calls)) * nstreams
+    for k in range(len(calls)):
+        calls[k]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(n):
+        calls[k % len(calls)]()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) * 1e6 / n
+    return {"streams": nstreams, "calls": n, "us_per_call": round(us, 2),
+            "positions_per_s": round(w.positions / (us * 1e-6), 1),
+            "hbm_frac": round(w.compulsory_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
 def graph_us_per_call(calls, reps=5):
