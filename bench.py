@@ -366,18 +366,20 @@ NGRAM = dict(B=512, capacity=8192, n_min=2, n_max=5, gamma=8, seed=77)
 
 def time_streams(sv, w, inputs, code, path, all_greedy, nstreams, steps):
     """Calls over independent batches, round-robin over `nstreams` streams (default
-    priority), each call with its own workspace and outputs, so that one call's chain of
-    dependent steps can overlap another's logit stream.  A context figure for serving loops
-    that keep several batches in flight; the step time above is one call after another."""
+    priority), each stream with its own workspace and outputs (calls on one stream run in
+    order), so that one call's chain of dependent steps can overlap another's logit stream.  A
+    context figure for serving loops that keep several batches in flight; the step time above
+    is one call after another."""
     import torch
     streams = [torch.cuda.Stream() for _ in range(nstreams)]
+    own = [(sv.alloc_workspace(w.B, w.gamma, w.V, code),
+            torch.empty(w.R_t, dtype=torch.int32, device="cuda"),
+            torch.empty(w.B, dtype=torch.int32, device="cuda")) for _ in range(nstreams)]
     ctl = sv.make_probe(path=path) if path else None
     calls = []
     for k in range(len(inputs) * nstreams):
         d, s = inputs[k % len(inputs)], streams[k % nstreams]
-        ws = sv.alloc_workspace(w.B, w.gamma, w.V, code)
-        out = torch.empty(w.R_t, dtype=torch.int32, device="cuda")
-        nacc = torch.empty(w.B, dtype=torch.int32, device="cuda")
+        ws, out, nacc = own[k % nstreams]
         if all_greedy:
             calls.append(sv.prepare_greedy(d["target"], d["tokens"], w.gamma, out, nacc, ws,
                                            cu_draft=d["cu"], probe=ctl, stream=s))
