@@ -741,3 +741,176 @@ def test_inverse_cdf_matches_searchsorted(T):
     assert clear.mean() > 0.99
     np.testing.assert_array_equal(got[clear], expect[clear])
     assert not np.isin(got, np.arange(0, V, 7)).any()
+
+
+# --------------------------------------------------------------------------- decision diagnostics
+#
+# The parity rule between the GPU and the oracle rests on three of the oracle's diagnostics:
+# the accept-test margin |u - p(x)/q(x)| at every decision up to the stop, the CDF gap of the
+# stop row's draw, and the residual mass sum_k max(p_k - q_k, 0) (wiki page, section
+# "数式で見る speculative decoding の正しさ": alpha(x) and p_corr; blent.ai page, section
+# "Pourquoi la qualité est préservée").  They are pinned twice: element by element against a
+# computation from scipy's softmax and numpy's cumsum / searchsorted, and by their meaning (a
+# uniform moved by less than the margin or gap leaves the oracle's output unchanged, one
+# moved past it changes it).
+
+def _reference_decisions(w, b):
+    """Request b's decisions from scipy softmax and numpy: (margins up to the stop, stop row,
+    weights drawn from, R, fallback, token, gap below u, gap above u)."""
+    T = float(w.temperatures[b])
+    tb, db, g = int(w.target_base[b]), int(w.draft_base[b]), int(w.gammas[b])
+    zt = workloads.decode(w.target[tb: tb + g + 1], w.dtype)
+    zd = workloads.decode(w.draft[db: db + g], w.dtype)
+    margins, stop = [], g
+    for i in range(g):
+        x = int(w.draft_tokens[db + i])
+        p = _softmax(zt[i], T)[x] if 0 <= x < w.V else 0.0
+        q = _softmax(zd[i], T)[x] if 0 <= x < w.V else 0.0
+        ratio = p / q if q > 0 else (np.inf if p > 0 else 0.0)
+        u = float(w.uniforms[tb + i, 0])
+        margins.append(abs(u - ratio))
+        if not u < ratio:
+            stop = i
+            break
+    p_stop = _softmax(zt[stop], T)
+    r = np.maximum(p_stop - _softmax(zd[stop], T), 0.0) if stop < g else p_stop
+    fallback = not r.sum() > 0
+    if fallback:
+        r = p_stop
+    R = r.sum()
+    u1 = float(w.uniforms[tb + stop, 1])
+    C = np.cumsum(r)
+    k = int(np.searchsorted(C, u1 * R, side="right"))
+    below = u1 - (C[k - 1] / R if k > 0 else 0.0)
+    above = C[k] / R - u1
+    return dict(margins=np.array(margins), stop=stop, R=R, fallback=fallback, token=k,
+                below=below, above=above)
+
+
+DIAG_CASES = [  # (B, gamma, V, dtype, seed, temperature, draft noise)
+    (40, 6, 300, "f32", 101, 1.0, 0.6),
+    (40, 5, 257, "bf16", 102, 0.7, 1.0),
+    (30, 8, 120, "f32", 103, 0.3, 0.2),
+    (30, 4, 500, "bf16", 104, 2.5, 1.5),
+]
+
+
+@pytest.mark.parametrize("B,gamma,V,dtype,seed,T,sigma", DIAG_CASES)
+def test_diagnostics_match_scipy_and_numpy(B, gamma, V, dtype, seed, T, sigma):
+    w = workloads.small(B=B, gamma=gamma, V=V, dtype=dtype, seed=seed, temperatures=T,
+                        draft_sigma=sigma, ragged=True)
+    w.draft_tokens[::11] = V        # outside the vocabulary: p = q = 0, ratio 0, rejected
+    r = oracle.verify(w)
+    for b in range(w.B):
+        ref = _reference_decisions(w, b)
+        db, g, n = int(w.draft_base[b]), int(w.gammas[b]), int(r["num_accepted"][b])
+        assert n == ref["stop"]
+        m = r["margin"][db: db + g]
+        np.testing.assert_allclose(m[: n + 1 if n < g else g], ref["margins"], rtol=1e-11,
+                                   atol=1e-13)
+        assert np.isnan(m[n + 1:]).all()     # nothing recorded past the stop
+        assert r["fallback"][b] == int(ref["fallback"])
+        assert r["resid_mass"][b] == pytest.approx(ref["R"], rel=1e-11, abs=1e-15)
+        assert r["cdf_gap"][b] == pytest.approx(min(ref["below"], ref["above"]), abs=1e-11)
+        if min(ref["below"], ref["above"]) > 1e-9:
+            assert r["out_tokens"][int(w.target_base[b]) + n] == ref["token"]
+
+
+def test_residual_mass_is_one_for_the_bonus_and_the_fallback():
+    # Every draft accepted (draft = target, accept uniforms 0): the bonus is drawn from p,
+    # whose mass is 1.  Draft = target and accept uniforms at the top: the first draft is
+    # rejected with p = q, the residual is empty, and the draw falls back to p (mass 1).
+    w = workloads.small(B=20, gamma=3, V=200, dtype="f32", seed=7, temperatures=0.8)
+    for b in range(w.B):
+        tb, db = int(w.target_base[b]), int(w.draft_base[b])
+        w.draft[db: db + 3] = w.target[tb: tb + 3]
+    w.uniforms[:, 0] = 0.0
+    r = oracle.verify(w)
+    assert (r["num_accepted"] == 3).all() and (r["fallback"] == 0).all()
+    np.testing.assert_allclose(r["resid_mass"], 1.0, rtol=1e-13)
+    w.uniforms[:, 0] = np.float32(np.nextafter(np.float32(1), np.float32(0)))
+    w.draft_tokens[:] = 0
+    w.target[:, 0] = w.target.max()      # token 0 has the row's largest p (= q): ratio 1
+    w.draft[:, 0] = w.target[0, 0]
+    r = oracle.verify(w)
+    assert (r["num_accepted"] == 3).all()     # ratio exactly 1 > u: accepted
+    w.draft_tokens[:] = 1                     # ratio 1 as well, but u = 1 - 2^-24 < 1 ...
+    w.uniforms[:, 0] = 1.0                    # ... so take u = 1: rejected, p = q, empty
+    r = oracle.verify(w)
+    assert (r["num_accepted"] == 0).all() and (r["fallback"] == 1).all()
+    np.testing.assert_allclose(r["resid_mass"], 1.0, rtol=1e-13)
+    for b in range(w.B):
+        assert min(_reference_decisions(w, b)["below"], _reference_decisions(w, b)["above"]) \
+            == pytest.approx(r["cdf_gap"][b], abs=1e-11)
+
+
+def _one(w, b):
+    tb, db, g = int(w.target_base[b]), int(w.draft_base[b]), int(w.gammas[b])
+    return Workload("one", w.dtype, 1, g, w.V, w.target[tb: tb + g + 1].copy(),
+                    w.draft[db: db + g].copy(), w.draft_tokens[db: db + g].copy(),
+                    w.uniforms[tb: tb + g + 1].copy(), w.temperatures[b: b + 1].copy(), None)
+
+
+def test_margin_is_the_distance_to_the_accept_boundary():
+    # Moving an accept uniform by half its margin toward the boundary leaves every decision
+    # as it was; moving it one and a half margins (past the boundary) flips that decision.
+    w = workloads.small(B=60, gamma=5, V=400, dtype="f32", seed=61, temperatures=0.9,
+                        draft_sigma=0.8, ragged=True)
+    r = oracle.verify(w)
+    flipped = 0
+    for b in range(w.B):
+        one = _one(w, b)
+        g, n = one.gamma, int(r["num_accepted"][b])
+        last = n if n < g else g - 1
+        for i in range(last + 1):
+            m = float(r["margin"][int(w.draft_base[b]) + i])
+            u = float(one.uniforms[i, 0])
+            if m < 1e-4:
+                continue
+            toward = -1.0 if i == n else 1.0     # rejected: u above the ratio; accepted: below
+            for scale, same in ((0.5, True), (1.5, False)):
+                v = u + toward * scale * m
+                if not 0.0 <= v < 1.0:
+                    continue
+                o = _one(w, b)
+                o.uniforms[i, 0] = np.float32(v)
+                n2 = int(oracle.verify(o)["num_accepted"][0])
+                if same:
+                    assert n2 == n, (b, i, scale)
+                else:
+                    assert (n2 > i) if i == n else (n2 == i), (b, i, scale, n, n2)
+                    flipped += 1
+    assert flipped > 40
+
+
+def test_cdf_gap_is_the_distance_to_the_nearest_cdf_step():
+    # Moving the draw's uniform by half the gap, either way, keeps the token; moving it by
+    # one and a half gaps toward the nearer CDF step gives the neighbouring token.  A gap
+    # taken on one side only fails where the other side's step is the nearer one.
+    w = workloads.small(B=80, gamma=3, V=60, dtype="f32", seed=62, temperatures=1.1,
+                        draft_sigma=1.2, ragged=True)
+    r = oracle.verify(w)
+    sides = {"below": 0, "above": 0}
+    for b in range(w.B):
+        ref = _reference_decisions(w, b)
+        gap = float(r["cdf_gap"][b])
+        if gap < 1e-4:
+            continue
+        tb, n = int(w.target_base[b]), int(r["num_accepted"][b])
+        tok = int(r["out_tokens"][tb + n])
+        u = float(w.uniforms[tb + n, 1])
+        near = "below" if ref["below"] <= ref["above"] else "above"
+        sign = -1.0 if near == "below" else 1.0
+        for delta, same in ((0.5 * gap, True), (-0.5 * gap, True), (1.5 * sign * gap, False)):
+            v = u + delta
+            if not 0.0 <= v < 1.0:
+                continue
+            o = _one(w, b)
+            o.uniforms[n, 1] = np.float32(v)
+            t2 = int(oracle.verify(o)["out_tokens"][n])
+            if same:
+                assert t2 == tok, (b, delta)
+            else:
+                assert (t2 < tok) if near == "below" else (t2 > tok), (b, near, tok, t2)
+                sides[near] += 1
+    assert sides["below"] > 5 and sides["above"] > 5
