@@ -21,7 +21,8 @@
  * Conventions fixed by this library where the pages leave a step open:
  *  - p = softmax(z_target / T_b), q = softmax(z_draft / T_b), one temperature per request;
  *    a request is sampled iff T_b > 0, greedy otherwise (T = 0 exactly is the pages' case).
- *    Temperatures below about 1.4e-38 act as that value.
+ *    Temperatures below about 1.4e-38 act as that value, and temperatures above about
+ *    1.7e24 (+inf included) as that one: p is then uniform over the unmasked tokens.
  *  - uniforms[r][0] is the accept test at draft position r (accept iff u < p(x)/q(x),
  *    strictly); uniforms[r][1] is the draw for the token emitted at target row r, used only
  *    at the stop row: the residual after a rejection, or the bonus from p at row gamma_b.

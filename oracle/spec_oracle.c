@@ -70,15 +70,23 @@ static void row_argmax(const void *base, int dtype, int64_t row, int64_t V,
   *idx_out = bi;
 }
 
-/* Softmax normaliser at temperature T: m = max_k z_k, S = sum_k exp((z_k - m) / T).  A masked
- * logit (-inf) contributes exp(-inf) = 0; a row needs one finite logit. */
+/* Unnormalised softmax weight exp((z - m) / T) of a logit z in a row whose maximum is m.  A
+ * masked logit (-inf) has weight 0 at every temperature: written out, because at T = +inf the
+ * quotient (-inf - m) / T is not a number. */
+static double weight(double z, double m, double T) {
+  if (z == -INFINITY) return 0.0;
+  return exp((z - m) / T);
+}
+
+/* Softmax normaliser at temperature T: m = max_k z_k, S = sum_k exp((z_k - m) / T); a row
+ * needs one finite logit. */
 static void row_softmax_stats(const void *base, int dtype, int64_t row, int64_t V, double T,
                               double *m_out, double *S_out) {
   double m;
   int64_t unused;
   row_argmax(base, dtype, row, V, &m, &unused);
   double S = 0.0;
-  for (int64_t k = 0; k < V; ++k) S += exp((logit_at(base, dtype, row * V + k) - m) / T);
+  for (int64_t k = 0; k < V; ++k) S += weight(logit_at(base, dtype, row * V + k), m, T);
   *m_out = m;
   *S_out = S;
 }
@@ -86,7 +94,7 @@ static void row_softmax_stats(const void *base, int dtype, int64_t row, int64_t 
 /* p_k = exp((z_k - m) / T) / S */
 static double prob(const void *base, int dtype, int64_t row, int64_t V, double T, double m,
                    double S, int64_t k) {
-  return exp((logit_at(base, dtype, row * V + k) - m) / T) / S;
+  return weight(logit_at(base, dtype, row * V + k), m, T) / S;
 }
 
 typedef struct {

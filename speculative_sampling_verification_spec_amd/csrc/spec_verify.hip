@@ -170,10 +170,15 @@ struct TempConst {
 
 // c = log2(e)/T as c_hi + c_lo with c_lo > 0 strictly (c_hi is c rounded down, one ulp lower
 // where c is a float): a masked logit z = -inf then gives z c_hi + z c_lo = -inf and a term of
-// exactly 0, never -inf + inf or -inf * 0.
+// exactly 0, never -inf + inf or -inf * 0.  c is kept in [2^-80, 1e38]: temperatures below
+// ~1.4e-38 act as ~1.4e-38, and above ~1.7e24 (T = +inf included) as ~1.7e24, where every
+// finite logit's term is 1 and the distribution is uniform over the unmasked tokens; at the
+// lower bound c_lo (~c 2^-24) is still a normal float.
+constexpr double kMinTempConst = 8.271806125530277e-25;  // 2^-80
 __device__ __forceinline__ TempConst temp_const(float T) {
   double c = kLog2e / (double)T;
-  if (c > 1e38) c = 1e38;  // temperatures below ~1.4e-38 act as ~1.4e-38
+  if (c > 1e38) c = 1e38;
+  if (!(c >= kMinTempConst)) c = kMinTempConst;
   float hi = (float)c;
   if ((double)hi >= c) hi = __uint_as_float(__float_as_uint(hi) - 1u);  // hi > 0: one ulp down
   const float lo = (float)(c - (double)hi);

@@ -328,8 +328,8 @@ def test_masked_logits(path, dtype):
     # Vocabulary masks (logit -inf, shared by a request's rows): 30% of the entries plus a run
     # of 20000, so some 16K tiles are masked whole; temperatures across the range (the
     # temperature constant's low part, kept positive, must not turn -inf into NaN)
-    temps = np.array([0.05, 0.3, 0.0, 0.7, 1.0, 1.3, 0.0, 2.5, 0.9, 0.6, 1.7, 0.45])
-    w = workloads.small(B=12, gamma=5, V=40000, dtype=dtype, seed=31, temperatures=temps,
+    temps = np.array([0.05, 0.3, 0.0, 0.7, 1.0, 1.3, 0.0, 2.5, 0.9, 0.6, 1.7, 0.45, np.inf])
+    w = workloads.small(B=13, gamma=5, V=40000, dtype=dtype, seed=31, temperatures=temps,
                         ragged=True, draft_sigma=0.8, mask_frac=0.3, mask_span=20000)
     _both(w, path=path)
     _both(w, greedy=True, path=path)
@@ -376,9 +376,10 @@ def test_single_token_vocabulary(path):
 @PATHS
 def test_extreme_temperatures(path):
     # tiny and huge T; with logits near +-10 the smaller temperatures take the row
-    # statistics' overflow-safe exponent form, the others the two-FMA form
-    temps = np.array([1e-30, 1e-6, 1e-3, 50.0, 1e4, 0.0], dtype=np.float32)
-    w = workloads.small(B=6, gamma=4, V=2048, dtype="bf16", seed=8, temperatures=temps)
+    # statistics' overflow-safe exponent form, the others the two-FMA form; T = +inf is the
+    # uniform distribution (every draft accepted, the bonus drawn uniformly)
+    temps = np.array([1e-30, 1e-6, 1e-3, 50.0, 1e4, 0.0, np.inf, 1e30], dtype=np.float32)
+    w = workloads.small(B=8, gamma=4, V=2048, dtype="bf16", seed=8, temperatures=temps)
     _both(w, path=path)
 
 

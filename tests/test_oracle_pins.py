@@ -914,3 +914,27 @@ def test_cdf_gap_is_the_distance_to_the_nearest_cdf_step():
                 assert (t2 < tok) if near == "below" else (t2 > tok), (b, near, tok, t2)
                 sides[near] += 1
     assert sides["below"] > 5 and sides["above"] > 5
+
+
+def test_infinite_temperature_is_uniform_over_unmasked_tokens():
+    # T = +inf: softmax(z / T) is uniform (its limit as T grows), so p = q = 1/V' over the V'
+    # unmasked tokens, every draft is accepted (ratio 1 > u) and the bonus is the inverse CDF
+    # of the uniform distribution, floor(u V') among the unmasked ids (numpy searchsorted).
+    for mask_frac in (0.0, 0.4):
+        w = workloads.small(B=30, gamma=4, V=333, dtype="bf16", seed=71, ragged=True,
+                            temperatures=np.inf, mask_frac=mask_frac)
+        r = oracle.verify(w)
+        assert (r["num_accepted"] == w.gammas).all()
+        zt = workloads.decode(w.target, "bf16")
+        for b in range(w.B):
+            tb, db, g = int(w.target_base[b]), int(w.draft_base[b]), int(w.gammas[b])
+            live = np.isfinite(zt[tb])
+            n_live = int(live.sum())
+            np.testing.assert_allclose(r["p_x"][db: db + g], 1.0 / n_live, rtol=1e-14)
+            np.testing.assert_allclose(r["q_x"][db: db + g], 1.0 / n_live, rtol=1e-14)
+            np.testing.assert_allclose(r["row_sum_t"][tb: tb + g + 1], n_live, rtol=1e-15)
+            u = float(w.uniforms[tb + g, 1])
+            C = np.cumsum(live.astype(np.float64) / n_live)
+            if r["cdf_gap"][b] > 1e-9:
+                assert r["out_tokens"][tb + g] == np.searchsorted(C, u * C[-1], side="right")
+            assert live[r["out_tokens"][tb + g]]

@@ -133,11 +133,17 @@ class Workload:
 _BLOCK = 256   # rows generated at a time, bounds host memory
 
 
+def _tempered(z: np.ndarray, T: float) -> np.ndarray:
+    """z / T, with masked logits (-inf) staying -inf at every temperature (T = +inf too)."""
+    with np.errstate(invalid="ignore"):
+        return np.where(np.isneginf(z), -np.inf, z / T)
+
+
 def _gumbel_max(z: np.ndarray, T: float, rng: np.random.Generator) -> int:
     u = rng.random(z.shape[-1])
     with np.errstate(divide="ignore"):
         g = -np.log(-np.log(u))
-    return int(np.argmax(z / T + g))
+    return int(np.argmax(_tempered(z, T) + g))
 
 
 def generate(*, name: str, B: int, V: int, dtype: str, gammas: Sequence[int], dense: bool,
@@ -305,7 +311,7 @@ def draw_draft_tokens(zd: np.ndarray, T: float, rng: np.random.Generator) -> np.
         u = rng.random(zd.shape)
         with np.errstate(divide="ignore"):
             g = -np.log(-np.log(u))
-        return np.argmax(zd / T + g, axis=-1).astype(np.int32)
+        return np.argmax(_tempered(zd, T) + g, axis=-1).astype(np.int32)
     return np.argmax(zd, axis=-1).astype(np.int32)
 
 
