@@ -83,17 +83,17 @@ enum {
  *  SPEC_PATH_ONE  one launch, a workgroup per row tile as in the first of the two launches;
  *                 B <= 2048.  Greedy calls (spec_verify_greedy): the last tile of a request to
  *                 finish merges and writes the request's outputs.  Sampling calls: a request's
- *                 tiles meet inside the launch (device-scope atomics and bounded polling),
- *                 split its stop row(s) between them, and the last one draws; all of the
- *                 call's workgroups (row slots x ceil(V / 16384)) must be resident on the
- *                 device at once (at most three quarters of the device's capacity for the
- *                 kernel).  A request whose workgroups do not all arrive within a bounded wait
- *                 (seconds; only if other work keeps them from being resident) comes back with
- *                 out_num_accepted = -1 (its token slots are then not valid), and the
- *                 workspace must be zero-filled again before its next use.
+ *                 tiles meet inside the launch (device-scope atomics), claim spans of its stop
+ *                 row(s), and the one completing the last span draws.  Tiles that arrive
+ *                 early wait, boundedly, to help; one whose wait runs out (other work keeps
+ *                 its siblings from being resident) leaves its share to the request's last
+ *                 arrival, which never waits, so the results never depend on the waits.
+ *                 Taken only if the call's workgroups (row slots x ceil(V / 16384)) fit in
+ *                 three quarters of the device's capacity for the kernel: beyond that the
+ *                 sharing would run mostly on one workgroup per request.
  *  SPEC_PATH_AUTO the library's choice, the default: one launch for calls of at most 2048 row
  *                 tiles with 16-byte aligned rows that it can take, where it measured faster
- *                 on MI355X; two launches otherwise.
+ *                 on MI355X; two launches otherwise.  Every path gives the same results.
  */
 #define SPEC_PATH_AUTO 0
 #define SPEC_PATH_TWO 1
@@ -121,9 +121,10 @@ typedef struct spec_probe {
                          touched                                                        */
   int path;           /* SPEC_PATH_AUTO, _TWO or _ONE; _ONE on a call that cannot take it,
                          or another value, returns SPEC_ERR_SHAPE                         */
-  unsigned int spin_limit; /* polls after which a bounded wait of the one-launch path gives
-                         up (0: the library's default, 2^22); a small value makes the
-                         time-out handling run, for tests of it                         */
+  unsigned int spin_limit; /* polls after which a waiting workgroup of the one-launch path
+                         stops waiting and leaves its share to the last arrival (0: the
+                         library's default, 2^12); a small value makes that hand-over run,
+                         for tests of it; results do not depend on it                   */
 } spec_probe;
 
 /*
@@ -141,8 +142,7 @@ typedef struct spec_probe {
  *  V              vocabulary size
  *  out_tokens     [R_t] int32      request b's slots 0..gamma_b: the n_b accepted drafts, the
  *                                  token emitted at the stop row n_b, then -1
- *  out_num_accepted [B] int32      n_b in [0, gamma_b]; the step emits n_b + 1 tokens (-1:
- *                                  the one-launch path gave up on the request, see above)
+ *  out_num_accepted [B] int32      n_b in [0, gamma_b]; the step emits n_b + 1 tokens
  *  workspace      device scratch of at least spec_verify_workspace_size(B, gamma, V, dtype)
  *                 bytes, 256-byte aligned, zero-filled before its first use; every call
  *                 leaves it ready for the next, of any shape.  Its first 512 KiB hold the
@@ -197,9 +197,9 @@ int spec_verify_greedy(const void *target_logits, int dtype, const int32_t *draf
  * to seq_tokens[b][seq_len[b] ..]; those at or past `capacity` are dropped and counted as
  * truncated; seq_len[b] becomes min(seq_len[b] + n_b + 1, capacity).  All pointers are device
  * pointers.  Errors: SPEC_ERR_SHAPE (B < 0, gamma outside [0, 64], capacity < 0), SPEC_ERR_NULL,
- * SPEC_ERR_HIP; B == 0 enqueues nothing.  A request whose n_b is -1 (the verification gave
- * up on it) is left unchanged and not counted.  Device data are not checked: n_b is clamped
- * to at most gamma_b and seq_len[b] to [0, capacity] for memory safety only.
+ * SPEC_ERR_HIP; B == 0 enqueues nothing.  Device data are not checked: for memory safety only,
+ * a request whose n_b is negative (outside the verification's output range) is left unchanged
+ * and not counted, n_b is clamped to at most gamma_b and seq_len[b] to [0, capacity].
  */
 int spec_verify_commit(const int32_t *out_tokens, const int32_t *out_num_accepted,
                        const int32_t *cu_draft, int32_t B, int32_t gamma, int32_t *seq_tokens,

@@ -292,21 +292,22 @@ int oracle_verify(const void *target, const void *draft, int dtype,
  * and count as truncated; the new length is min(seq_len[b] + n_b + 1, capacity).  stats (may
  * be NULL) accumulates {proposed = sum gamma_b, accepted = sum n_b, emitted = sum (n_b + 1),
  * requests = B, truncated}; hist (may be NULL, gamma + 1 bins) counts requests by n_b.
- * An accepted count of -1 is the verification's report that the request gave up (a bounded
- * wait of its one-launch path ran out): such a request is left as it is and not counted.
- * Returns 0, or -1 on bad sizes or an accepted count outside [-1, gamma_b].
+ * Returns 0, or -1 (nothing written) on bad sizes or an accepted count outside [0, gamma_b] (a
+ * verification step accepts between 0 and gamma_b drafts).
  */
 int oracle_commit(const int32_t *out_tokens, const int32_t *num_accepted,
                   const int32_t *cu_draft, int32_t B, int32_t gamma, int32_t *seq_tokens,
                   int64_t capacity, int32_t *seq_len, uint64_t *stats, uint64_t *hist) {
   if (B < 0 || gamma < 0 || capacity < 0) return -1;
+  for (int32_t b = 0; b < B; ++b) {  /* every count checked before anything is written */
+    int64_t gb = cu_draft ? (int64_t)cu_draft[b + 1] - cu_draft[b] : gamma;
+    if (gb < 0 || gb > gamma || num_accepted[b] < 0 || num_accepted[b] > gb) return -1;
+  }
   for (int32_t b = 0; b < B; ++b) {
     int64_t dbase = cu_draft ? cu_draft[b] : (int64_t)b * gamma;
     int64_t gb = cu_draft ? (int64_t)cu_draft[b + 1] - cu_draft[b] : gamma;
     int64_t tbase = dbase + b;
     int64_t n = num_accepted[b];
-    if (gb < 0 || gb > gamma || n < -1 || n > gb) return -1;
-    if (n == -1) continue;
     int64_t len = seq_len[b];
     uint64_t lost = 0;
     for (int64_t i = 0; i <= n; ++i) {

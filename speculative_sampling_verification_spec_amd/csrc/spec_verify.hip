@@ -36,10 +36,11 @@
 //  k_greedy1   Greedy calls: k_rowstats' tiles over the target rows; the last tile of a
 //              request to finish merges the request's partials and writes its outputs.
 //
-//  k_onepass   Sampling calls whose workgroups all fit on the device at once: k_rowstats'
-//              tiles over every row; the request's tiles meet on an arrival counter (bounded
-//              polling), then each merges and tests, sums its share of the stop row(s), and
-//              the last to finish draws, as k_finish does.
+//  k_onepass   Sampling calls whose workgroups fit on the device at once: k_rowstats' tiles
+//              over every row; the request's tiles meet on an arrival counter, sum one span of
+//              the stop row(s) each, and the one completing the last span draws, as k_finish
+//              does.  Waits are bounded and a workgroup that stops waiting hands its span to
+//              the last arrival, so no wait can change a result.
 //
 // Per-request counters sit one per 128-byte line: atomics on one line serialise.
 //
@@ -78,8 +79,10 @@ constexpr int kChunkUnits = 64;              // residual sums: one per 64 units 
 constexpr int kOneMaxB = 2048;               // requests the one-launch counters cover
 constexpr int kCounterStride = 32;           // one counter per 128-byte line: atomics on a line
                                              // serialise, so requests must not share one
-constexpr uint32_t kSpinLimit = 1u << 22;    // default polls before a one-launch workgroup
-                                             // stops waiting
+constexpr uint32_t kSpinLimit = 1u << 12;    // default polls before a one-launch workgroup
+                                             // stops waiting (a poll is a device-scope round
+                                             // trip, ~1 us: milliseconds, where a request's
+                                             // tiles arrive within microseconds)
 constexpr int64_t kMaxV = int64_t(1) << 24;
 constexpr double kLog2e = 1.4426950408889634074;
 constexpr size_t kAlign = 256;
@@ -132,8 +135,9 @@ struct Params {
   int64_t chunk_stride;
   uint32_t *done;           // k_finish slices of request b finished, at [b * kCounterStride]
                             // (k_rowstats clears it)
-  uint32_t *arrive, *odone; // one-launch counters, request b's at [b * kCounterStride]: zero
-                            // before and after every call
+  uint32_t *arrive, *odone; // one-launch counters, request b's at [b * kCounterStride]
+                            // (arrive: a 64-bit word, arrivals and spans handed over; odone:
+                            // completed spans): zero before and after every call
   int32_t nslice;           // k_finish workgroups per request
   int64_t slice_units;      // stop-row units per k_finish workgroup (a multiple of 64)
   int32_t spr;              // row slots per request: 2*gamma+1 (sample) or gamma+1 (greedy)
@@ -835,15 +839,12 @@ struct ReqLds {
 //  2. accept tests lane-parallel on wavefront 0 (p(x), q(x) in fp64 from the logits that
 //     k_rowstats captured) and the first rejection by ballot + find-first-set.
 // Merged rows sit in L by row slot (target row r at r, draft row i at gamma + 1 + i).  With
-// `write`, the outputs and the row probes are written (out_num_accepted only with `write_n`:
-// the one-launch path leaves a sampled request's count to the workgroup that draws, so that a
-// timed-out request keeps -1).  Ends with a barrier; the stop row is
+// `write`, the outputs and the row probes are written.  Ends with a barrier; the stop row is
 // in L.j.  Returns the request's temperature constant.  SHARED: the partials and slot records
 // were written by other workgroups of the same launch.
 template <int NT, bool SHARED>
 __device__ __forceinline__ TempConst finish_head(const Params &P, int32_t b, bool write, ReqLds &L,
-                                 int64_t &dbase, int32_t &gb, bool &sampling,
-                                 bool write_n = true) {
+                                 int64_t &dbase, int32_t &gb, bool &sampling) {
   constexpr int NW = NT / 64;
   constexpr int G = 4;  // rounds of row slots whose partials are loaded at once
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -973,7 +974,7 @@ __device__ __forceinline__ TempConst finish_head(const Params &P, int32_t b, boo
       if (lane == 0) {
         if (j < gb) P.out_tokens[tbase + gb] = -1;
         if (!sampling) P.out_tokens[tbase + j] = L.i[j];
-        if (write_n) P.out_n[b] = j;
+        P.out_n[b] = j;
       }
       if (sampling && lane < gb) {
         if (P.p_x) P.p_x[dbase + lane] = p;
@@ -1301,20 +1302,36 @@ __global__ __launch_bounds__(kRsThreads) void k_greedy1(Params P) {
 
 // ------------------------------------------------------------------ k_onepass
 
+// A request's one-launch counters back to zero: the 64-bit arrival word and the completed
+// spans.
+__device__ __forceinline__ void reset_request_counters(unsigned long long *word, uint32_t *done) {
+  __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // The whole step in one launch, for small calls.  Workgroups (tile, row slot) as k_rowstats:
 // each computes its tile's statistics, hands the partial over with device-scope atomic stores,
-// waits for them to complete and adds itself to its request's arrival counter.
+// waits for them to complete and counts itself in on its request's 64-bit arrival word (low
+// half: arrivals; high half: spans handed over), whose old value gives its arrival rank.
 //  - A greedy request (T = 0) is finished by its last arrival: merge and comparisons, as
-//    k_finish's slice 0.  Nothing waits, so greedy calls take any grid.
-//  - The workgroups of a sampled request poll the counter (bounded: kSpinLimit polls) until
-//    all of the request's tiles are in, so the call's workgroups must all be resident at once
-//    (the host checks the device's capacity for this kernel).  Each then merges and tests (the
-//    request's first tile writes the outputs), sums its share of the stop row(s) into chunk
-//    sums, and adds itself to a second counter; the last one draws, as in k_finish.
-// The last user of each counter returns it to zero.  A request whose workgroups do not all
-// arrive within the bound (only possible if they could not all be resident) is reported with
-// out_num_accepted = -1: a workgroup that gives up writes it, and a sampled request's count is
-// written only by the workgroup that draws, which a request with a time-out never reaches.
+//    k_finish's slice 0.  Nothing waits.
+//  - A sampled request's stop row(s) are cut into spans of whole 64-unit chunks, at most one
+//    per tile and at most 32; the workgroup of arrival rank r owns span r.  An owner that is
+//    not the last arrival waits (bounded polling) for the request's last tile, then merges and
+//    tests (every workgroup reaches the same decision from the same partials) and sums its
+//    span.  The last arrival merges, tests, writes the outputs and sums its own span, if any.
+//    A span's chunk sums are published before its completion is counted, and the workgroup
+//    whose count completes the last span draws, as k_finish's last slice does.
+//  - An owner whose bound runs out (its siblings are not all resident: other work holds the
+//    device) hands its span over by adding its bit to the high half of the arrival word.  The
+//    last arrival's own arrival returns the spans handed over before it, and it sums those as
+//    well; an owner whose hand-over finds every tile already in has handed nothing (the last
+//    arrival read the word before) and goes on.  So the waits decide only who sums a span,
+//    never a result, and every span is summed exactly once.
+//  - Every other touch of a request's counters (arrivals, polls and hand-overs by owners, each
+//    followed by that owner's completion or exit) happens before the count completes, so the
+//    drawing workgroup returns the counters to zero before it draws: every call leaves them
+//    as it found them.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kRsThreads) void k_onepass(Params P) {
   using U = Unit<DT, VEC>;
@@ -1326,6 +1343,8 @@ __global__ __launch_bounds__(kRsThreads) void k_onepass(Params P) {
   __shared__ ReqLds L;
   __shared__ DrawLds<kWaves> D;
   __shared__ int32_t s_go;
+  __shared__ uint32_t s_rank;
+  __shared__ uint32_t s_handed;
   const int tid = threadIdx.x;
   const uint32_t slot = blockIdx.y + blockIdx.z * gridDim.y;
   const uint32_t spr = (uint32_t)P.spr;
@@ -1337,21 +1356,18 @@ __global__ __launch_bounds__(kRsThreads) void k_onepass(Params P) {
   float T;
   request(P, b, dbase, gb, T);
   const bool sampling = T > 0.f;
-  // live row r of the request: target rows 0..gb (slot r), then draft rows (slot gamma+1+i)
-  int32_t r;
+  // the row of slot k: target rows 0..gb (slot k), then draft rows (slot gamma+1+i)
   const void *base;
   int64_t row;
   int32_t pos;
   if (k <= P.gamma) {
     if (k > gb) return;
-    r = k;
     base = P.target;
     row = dbase + b + k;
     pos = k;
   } else {
     const int32_t i = k - P.gamma - 1;
     if (i >= gb || !sampling) return;
-    r = gb + 1 + i;
     base = P.draft;
     row = dbase + i;
     pos = i;
@@ -1378,66 +1394,79 @@ __global__ __launch_bounds__(kRsThreads) void k_onepass(Params P) {
   // Arrival: this workgroup's stores are complete before it counts itself in.
   const int32_t nrows = gb + 1 + (sampling ? gb : 0);
   const uint32_t n = (uint32_t)nrows * (uint32_t)P.nsplit;  // the request's tiles
-  const int32_t w = r * P.nsplit + (int32_t)blockIdx.x;        // this tile among them
+  // Spans of whole 64-unit chunks, at most one per tile and at most 32.
+  const int64_t nunits = (P.V + W - 1) / W;
+  const int64_t most = n < 32u ? (int64_t)n : 32;
+  const int64_t su = ceil_div_dev(ceil_div_dev(nunits, most), kChunkUnits) * kChunkUnits;
+  const uint32_t nspans = (uint32_t)ceil_div_dev(nunits, su);
   wait_memory();
   __syncthreads();
-  uint32_t *arrive = &P.arrive[b * kCounterStride];
+  // Request b's arrival word (its 128-byte line of `arrive`) and completed spans (its line of
+  // `odone`).
+  unsigned long long *word =
+      reinterpret_cast<unsigned long long *>(&P.arrive[b * kCounterStride]);
+  uint32_t *done = &P.odone[b * kCounterStride];
   if (tid == 0) {
-    const uint32_t old =
-        __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int32_t go = old == n - 1u ? 2 : 1;  // 2: the last arrival
-    if (go == 1 && sampling) {
+    const unsigned long long was =
+        __hip_atomic_fetch_add(word, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t rank = (uint32_t)was;
+    int32_t go;  // 2: the last arrival; 1: an owner that goes on; 0: nothing (more) to do
+    if (rank == n - 1u) {
+      go = 2;
+    } else if (!sampling || rank >= nspans) {
+      go = 0;
+    } else {
+      go = 1;
       uint32_t spins = 0;
-      while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n) {
+      while ((uint32_t)__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n) {
         __builtin_amdgcn_s_sleep(1);
-        if (++spins == P.spin_limit) {
-          go = -1;
+        if (++spins == P.spin_limit) {  // hand the span over, unless the last tile is in
+          const unsigned long long now = __hip_atomic_fetch_add(
+              word, 1ull << (32 + rank), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          go = (uint32_t)now == n ? 1 : 0;
           break;
         }
       }
     }
     s_go = go;
+    s_rank = rank;
+    s_handed = go == 2 ? (uint32_t)(was >> 32) : 0u;
   }
   __syncthreads();
   const int32_t go = s_go;
-  if (!sampling && go != 2) return;  // a greedy request: only its last arrival goes on
-  if (go < 0) {
-    if (tid == 0) P.out_n[b] = -1;
-    return;
-  }
-  if (!sampling && tid == 0)
-    __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (go == 0) return;
   int64_t db;
   int32_t g;
   bool smp;
-  const TempConst tc =
-      finish_head<kThreads, true>(P, b, !sampling || w == 0, L, db, g, smp, !sampling);
-  if (!sampling) return;
+  if (!sampling) {  // a greedy request: its last arrival finishes it
+    if (tid == 0) __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    finish_head<kThreads, true>(P, b, true, L, db, g, smp);
+    return;
+  }
+  const TempConst tc = finish_head<kThreads, true>(P, b, go == 2, L, db, g, smp);
   const Stop st = make_stop(L, gb, P.gamma + 1, tc, dbase + b + L.j, dbase + L.j);
-  // This tile's share of the stop row(s): whole 64-unit chunks, spread over the request's n
-  // tiles (some shares may be empty).
-  const int64_t nunits = (P.V + W - 1) / W;
-  const int64_t su = ceil_div_dev(ceil_div_dev(nunits, (int64_t)n), kChunkUnits) * kChunkUnits;
-  const int64_t ub = (int64_t)w * su;
-  const int64_t ue = ub + su < nunits ? ub + su : nunits;
   double *cs = P.chunk_sums + (int64_t)b * P.chunk_stride;
-  if (ub < ue) stream_chunks<DT, VEC, kThreads, kFinRU>(P, st, ub, ue, cs);
+  uint32_t mine = s_handed;  // spans this workgroup sums: its own, and those handed over
+  if (s_rank < nspans) mine |= 1u << s_rank;
+  if (mine == 0) return;     // the last arrival without a span: the outputs were its part
+  const uint32_t count = (uint32_t)__popc(mine);
+  while (mine) {
+    const int32_t c = __ffs((int)mine) - 1;
+    mine &= mine - 1u;
+    const int64_t ub = (int64_t)c * su;
+    const int64_t ue = ub + su < nunits ? ub + su : nunits;
+    stream_chunks<DT, VEC, kThreads, kFinRU>(P, st, ub, ue, cs);
+  }
   wait_memory();
   __syncthreads();
-  uint32_t *odone = &P.odone[b * kCounterStride];
-  if (tid == 0)
-    s_go = __hip_atomic_fetch_add(odone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-           n - 1u;
-  __syncthreads();
-  if (!s_go) return;
   if (tid == 0) {
-    __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(odone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // Only a request all of whose workgroups finished gets its count; after a time-out
-    // nothing draws and the -1 stays.
-    P.out_n[b] = L.j;
+    const uint32_t before =
+        __hip_atomic_fetch_add(done, count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_go = before + count == nspans;
+    if (s_go) reset_request_counters(word, done);
   }
-  draw_token<DT, VEC, kThreads>(P, b, st, cs, D);
+  __syncthreads();
+  if (s_go) draw_token<DT, VEC, kThreads>(P, b, st, cs, D);  // every span's chunk sums are in
 }
 
 // ------------------------------------------------------------------ k_commit
@@ -1454,7 +1483,8 @@ struct CommitParams {
 // One thread per request: append the request's n_b + 1 emitted tokens to its history at
 // seq_len[b], clamp the length at capacity, and fold the step into the counters (wavefront
 // sums and an LDS histogram, then one device atomic per counter and bin per workgroup).  A
-// request whose count is negative (-1: its verification gave up) is left alone, uncounted.
+// count outside the verification's range is device data the host cannot check: a negative one
+// leaves the request alone and uncounted, one above gamma_b is clamped (memory safety only).
 __global__ __launch_bounds__(kThreads) void k_commit(CommitParams C) {
   __shared__ unsigned long long s_sum[5][kWaves];
   __shared__ uint32_t s_hist[SPEC_MAX_GAMMA + 1];

@@ -476,20 +476,16 @@ def test_commit_of_a_greedy_step_appends_target_argmax_decoding():
         np.testing.assert_array_equal(seq[b, L: L + len(ref)], ref)
 
 
-def test_commit_leaves_requests_that_gave_up():
-    # a count of -1 (the verification gave up on the request) appends nothing and counts
-    # nothing; the other request commits as usual
+def test_commit_rejects_counts_outside_the_step():
+    # a step accepts between 0 and gamma_b drafts: any other count is refused, nothing written
     out = np.array([7, 8, 9, 4, 5, -1], dtype=np.int32)   # two requests, gamma 2
-    nacc = np.array([-1, 1], dtype=np.int32)
     seq = np.zeros((2, 10), dtype=np.int32)
     ln = np.array([3, 2], dtype=np.int32)
-    stats = np.zeros(5, dtype=np.uint64)
-    hist = np.zeros(3, dtype=np.uint64)
-    oracle.commit(out, nacc, 2, seq, ln, stats=stats, hist=hist)
-    assert list(ln) == [3, 4] and (seq[0] == 0).all() and list(seq[1, 2:4]) == [4, 5]
-    assert list(stats) == [2, 1, 2, 1, 0] and list(hist) == [0, 1, 0]
-    with pytest.raises(ValueError):
-        oracle.commit(out, np.array([-2, 1], dtype=np.int32), 2, seq, ln)
+    for bad in ([-1, 1], [3, 1], [0, -2]):
+        with pytest.raises(ValueError):
+            oracle.commit(out, np.array(bad, dtype=np.int32), 2, seq, ln)
+    oracle.commit(out, np.array([0, 1], dtype=np.int32), 2, seq, ln)
+    assert list(ln) == [4, 4] and seq[0, 3] == 7 and list(seq[1, 2:4]) == [4, 5]
 
 
 def test_commit_truncates_at_capacity_and_never_writes_past_it():
