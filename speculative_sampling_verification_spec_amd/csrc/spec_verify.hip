@@ -789,6 +789,55 @@ __device__ __forceinline__ float resid_unit(const typename Unit<DT, VEC>::Store 
   return unit_sum<W>(r);
 }
 
+// Residual weights of a stop row whose residual is small, without forming p - q: for
+// delta_k = log2(q_k / p_k) = (zd_k - zt_k) c + kd (kd: the maxima's and normalisers' part,
+// folded into one float), S_t (p_k - q_k) = e_t,k (1 - 2^delta_k), and where |delta| < 1 the
+// factor 1 - 2^delta is taken by expm1, so the term keeps its relative accuracy however close
+// q_k is to p_k (the logit difference is exact, or correctly rounded, in fp32, and delta is
+// small exactly when the term is).  Elsewhere the term is e_t,k - 2^(a_k + delta_k), a_k the
+// exponent argument of e_t,k, which cannot overflow.  A masked target entry (e_t = 0) gives 0.
+constexpr float kLn2f = 0.69314718055994531f;
+__device__ __forceinline__ float acc_term(float zt, float zd, const Stop &st, float kd,
+                                          float &et) {
+  const float a = arg_shifted(zt, st.mt, st.c_hi, st.c_lo);
+  et = ex2(a);
+  const float dz = zd - zt;
+  const float dl = fmaf(dz, st.c_hi, fmaf(dz, st.c_lo, kd));
+  if (!(et > 0.f)) return 0.f;
+  if (fabsf(dl) < 1.f) return -et * expm1f(dl * kLn2f);
+  return et - ex2(a + dl);
+}
+template <int W>
+__device__ __forceinline__ void resid_weights_acc(const float (&zt)[W], const float (&zd)[W],
+                                                  const Stop &st, float kd, float (&r)[W]) {
+#pragma unroll
+  for (int q = 0; q < W; ++q) {
+    float et;
+    const float v = acc_term(zt[q], zd[q], st, kd, et);
+    r[q] = v > 0.f ? v : 0.f;
+  }
+}
+
+// Weights and pairwise sum of unit u of the stop row(s): the ordinary form, or (ACC) the
+// relatively accurate one of a small residual.
+template <int DT, bool VEC, bool ACC>
+__device__ __forceinline__ float unit_weights(const typename Unit<DT, VEC>::Store *tr,
+                                              const typename Unit<DT, VEC>::Store *dr, int64_t u,
+                                              const Stop &st, float kd,
+                                              float (&r)[Unit<DT, VEC>::W]) {
+  using U = Unit<DT, VEC>;
+  constexpr int W = U::W;
+  if constexpr (!ACC) {
+    return resid_unit<DT, VEC>(tr, dr, u, st, r);
+  } else {
+    float zt[W], zd[W];
+    U::cvt(U::template load<false>(tr, u), zt);
+    U::cvt(U::template load<false>(dr, u), zd);
+    resid_weights_acc<W>(zt, zd, st, kd, r);
+    return unit_sum<W>(r);
+  }
+}
+
 // Draw from p over a whole target row (used only when the residual is empty after rounding).
 template <int DT, int NT>
 __device__ int32_t draw_from_row(const void *tr, int64_t V, const Stop &st, double u,
@@ -1023,9 +1072,9 @@ __device__ __forceinline__ Stop make_stop(const ReqLds &L, int32_t gb, int32_t d
 // pass in flight (ordinary loads: nontemporal ones here measured a slower row-statistics stream
 // in the next call); one fp64 sum per 64-unit chunk (one wavefront-wide load) into cs.  ub is a
 // multiple of 64 units, so every chunk is summed by one wavefront.
-template <int DT, bool VEC, int NT, int RU>
+template <int DT, bool VEC, int NT, int RU, bool ACC = false>
 __device__ __forceinline__ void stream_chunks(const Params &P, const Stop &st, int64_t ub,
-                                              int64_t ub_end, double *cs) {
+                                              int64_t ub_end, double *cs, float kd = 0.f) {
   using U = Unit<DT, VEC>;
   using Store = typename U::Store;
   constexpr int W = U::W;
@@ -1048,7 +1097,10 @@ __device__ __forceinline__ void stream_chunks(const Params &P, const Stop &st, i
       float zt[W], zd[W], r[W];
       U::cvt(rt[q], zt);
       U::cvt(rd[q], zd);
-      resid_weights<W>(zt, zd, st, r);
+      if constexpr (ACC)
+        resid_weights_acc<W>(zt, zd, st, kd, r);
+      else
+        resid_weights<W>(zt, zd, st, r);
       const float us = unit_sum<W>(r);
       const double sum = wave_sum(c0 + lane < ub_end ? (double)us : 0.0);
       if (lane == 0) share_store(&cs[c0 / kChunkUnits], sum);
@@ -1060,19 +1112,28 @@ __device__ __forceinline__ void stream_chunks(const Params &P, const Stop &st, i
 template <int NW>
 struct DrawLds {
   double shd[NW];
+  double acc[2][NW];
   int32_t shi[NW];
   int32_t c, tok;
   double local;
 };
 
-// Step 4, the draw, by a workgroup of NT threads once every chunk sum of request b is in cs
-// (written by other workgroups, so read with device-scope loads):
-// a block scan over the chunk sums picks the chunk holding u * R, a wavefront scan over its
-// 64 units picks the unit, and a walk over the unit's elements gives the token.
-template <int DT, bool VEC, int NT>
-__device__ __forceinline__ void draw_token(const Params &P, int32_t b, const Stop &st,
-                                           const double *cs,
-                           DrawLds<NT / 64> &D) {
+// Below this residual mass (relative to the row's normaliser) the draw is recomputed in the
+// accurate form.  The ordinary weights (e_t - rho e_d)_+ carry the error of rho = S_t / S_d,
+// whose two fp32-term normalisers are each within ~2e-7 relative: an absolute error of at most
+// ~3e-7 in the mass and of ~3e-7 / R in the draw's normalised running sum.  Above 0.05 that is
+// within 1e-5 relative for the mass and a few 1e-6 at worst (~1e-7 typically) for the draw.
+constexpr double kAccurateBelow = 0.05;
+constexpr int kAccRU = 2;
+
+// Pick the token from the chunk sums cs of the stop row(s), by a workgroup of NT threads: a
+// block scan over the chunk sums picks the chunk holding u * R, a wavefront scan over its 64
+// units picks the unit, and a walk over the unit's elements gives the token (into D.tok, -1 if
+// every weight is 0).  R: the total.  The chunk sums
+// were written by other workgroups (or this one), so they are read with device-scope loads.
+template <int DT, bool VEC, int NT, bool ACC>
+__device__ void draw_pick(const Params &P, const Stop &st, float kd, const double *cs,
+                          double u, DrawLds<NT / 64> &D, double &R) {
   using U = Unit<DT, VEC>;
   using Store = typename U::Store;
   constexpr int W = U::W;
@@ -1080,7 +1141,6 @@ __device__ __forceinline__ void draw_token(const Params &P, int32_t b, const Sto
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const Store *tr = static_cast<const Store *>(row_ptr<DT>(P.target, st.trow, P.V));
   const Store *dr = static_cast<const Store *>(row_ptr<DT>(P.draft, st.drow, P.V));
-  const double u = (double)P.uniforms[2 * st.trow + 1];
   const int64_t nunits = (P.V + W - 1) / W;
   const int64_t nchunks = (nunits + 63) / 64;
 
@@ -1102,7 +1162,6 @@ __device__ __forceinline__ void draw_token(const Params &P, int32_t b, const Sto
   } else {
     for (int64_t c = a; c < e_; ++c) mine += share_load(&cs[c]);
   }
-  double R;
   const double before = block_excl_scan<NW>(mine, D.shd, R);
   const double target = u * R;
   const int32_t first = block_first<NW>(mine > 0.0 && before + mine > target, D.shi);
@@ -1154,47 +1213,117 @@ __device__ __forceinline__ void draw_token(const Params &P, int32_t b, const Sto
   }
   __syncthreads();
   const int32_t csel = D.c;
-  if (csel >= 0) {
-    if (wave == 0) {
-      // The chunk's 64 units: a wavefront scan picks the unit, its lane walks the elements.
-      // With no crossing (u at the far end), the last unit with mass is taken.
-      const int64_t uu = (int64_t)csel * 64 + lane;
-      float r[W];
-      float us = 0.f;
-      if (uu < nunits) us = resid_unit<DT, VEC>(tr, dr, uu, st, r);
-      const double local = D.local;
-      const double incl = wave_incl_scan((double)us);
-      const uint64_t cross = __ballot(us > 0.f && incl > local);
-      const uint64_t pos = __ballot(us > 0.f);
-      const int32_t pl = cross ? __ffsll((long long)cross) - 1
-                               : (pos ? 63 - __clzll((long long)pos) : -1);
-      if (lane == pl) {
-        double run = incl - (double)us;
-        int32_t tok = -1, lastpos = -1;
-        for (int e = 0; e < W; ++e) {
-          if (r[e] > 0.f) {
-            lastpos = (int32_t)(uu * W + e);
-            run += (double)r[e];
-            if (cross && tok < 0 && run > local) tok = lastpos;
-          }
+  if (csel >= 0 && wave == 0) {
+    // The chunk's 64 units: a wavefront scan picks the unit, its lane walks the elements.
+    // With no crossing (u at the far end), the last unit with mass is taken.
+    const int64_t uu = (int64_t)csel * 64 + lane;
+    float r[W];
+    float us = 0.f;
+    if (uu < nunits) us = unit_weights<DT, VEC, ACC>(tr, dr, uu, st, kd, r);
+    const double local = D.local;
+    const double incl = wave_incl_scan((double)us);
+    const uint64_t cross = __ballot(us > 0.f && incl > local);
+    const uint64_t pos = __ballot(us > 0.f);
+    const int32_t pl = cross ? __ffsll((long long)cross) - 1
+                             : (pos ? 63 - __clzll((long long)pos) : -1);
+    if (lane == pl) {
+      double run = incl - (double)us;
+      int32_t tok = -1, lastpos = -1;
+      for (int e = 0; e < W; ++e) {
+        if (r[e] > 0.f) {
+          lastpos = (int32_t)(uu * W + e);
+          run += (double)r[e];
+          if (cross && tok < 0 && run > local) tok = lastpos;
         }
-        D.tok = tok >= 0 ? tok : lastpos;
       }
+      D.tok = tok >= 0 ? tok : lastpos;
     }
+  }
+  __syncthreads();
+}
+
+// Normaliser sums of the stop row(s) in the accurate form, over the whole row by one
+// workgroup: St = sum e_t,k and Dd = sum e_t,k (1 - 2^delta0_k), delta0_k = (zd - zt) c + kd0
+// = log2(e_d,k / e_t,k), so that S_d (in e_t's shift) is St - Dd with Dd as accurate as its
+// terms.
+template <int DT, bool VEC, int NT, int RU>
+__device__ void accurate_sums(const Params &P, const Stop &st, float kd0, DrawLds<NT / 64> &D,
+                              double &St, double &Dd) {
+  using U = Unit<DT, VEC>;
+  using Store = typename U::Store;
+  constexpr int W = U::W;
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x;
+  const Store *tr = static_cast<const Store *>(row_ptr<DT>(P.target, st.trow, P.V));
+  const Store *dr = static_cast<const Store *>(row_ptr<DT>(P.draft, st.drow, P.V));
+  const int64_t nunits = (P.V + W - 1) / W;
+  double s_t = 0.0, s_d = 0.0;
+  for (int64_t ub = 0; ub < nunits; ub += (int64_t)NT * RU) {
+    typename U::Raw rt[RU], rd[RU];
+#pragma unroll
+    for (int q = 0; q < RU; ++q) {
+      const int64_t u = ub + q * NT + tid;
+      rt[q] = u < nunits ? U::template load<false>(tr, u) : U::filler();
+      rd[q] = u < nunits ? U::template load<false>(dr, u) : U::filler();
+    }
+#pragma unroll
+    for (int q = 0; q < RU; ++q) {
+      float zt[W], zd[W], et[W], gt[W];
+      U::cvt(rt[q], zt);
+      U::cvt(rd[q], zd);
+#pragma unroll
+      for (int k = 0; k < W; ++k) gt[k] = acc_term(zt[k], zd[k], st, kd0, et[k]);
+      s_t += (double)unit_sum<W>(et);
+      s_d += (double)unit_sum<W>(gt);
+    }
+  }
+  St = block_sum1<NW>(s_t, D.acc[0]);
+  Dd = block_sum1<NW>(s_d, D.acc[1]);
+}
+
+// Step 4, the draw, by a workgroup of NT threads once every chunk sum of request b is in cs.
+// A residual whose mass is small is drawn again in the accurate form: normalisers from the stop
+// rows' own terms, then chunk sums of the accurate weights written over cs, then the same
+// pick.
+template <int DT, bool VEC, int NT>
+__device__ __forceinline__ void draw_token(const Params &P, int32_t b, const Stop &st, double *cs,
+                                           DrawLds<NT / 64> &D) {
+  using U = Unit<DT, VEC>;
+  constexpr int W = U::W;
+  const double u = (double)P.uniforms[2 * st.trow + 1];
+  double R;
+  draw_pick<DT, VEC, NT, false>(P, st, 0.f, cs, u, D, R);
+  double norm = st.st;  // the normaliser R is divided by for the probe
+  if (st.mode == kModeResidual && R < kAccurateBelow * st.st) {
+    // log2(e_d / e_t) = (zd - zt) c + kd0, kd0 = -(md - mt) c
+    const double c = (double)st.c_hi + (double)st.c_lo;
+    const double kd0 = -((double)st.md - (double)st.mt) * c;
+    double St, Dd;
+    // (kAccRU units per thread and pass: this rare path must not raise the kernel's registers)
+    accurate_sums<DT, VEC, NT, kAccRU>(P, st, (float)kd0, D, St, Dd);
+    // delta_k = log2(q_k / p_k) = log2(e_d,k / e_t,k) + log2(S_t / S_d), S_d = St - Dd
+    const double kd = kd0 - log1p(-Dd / St) / 0.69314718055994531;
+    stream_chunks<DT, VEC, NT, kAccRU, true>(P, st, 0, (P.V + W - 1) / W, cs, (float)kd);
+    wait_memory();
     __syncthreads();
-    if (tid == 0) {
+    draw_pick<DT, VEC, NT, true>(P, st, (float)kd, cs, u, D, R);
+    norm = St;
+  }
+  if (D.tok >= 0) {
+    if (threadIdx.x == 0) {
       P.out_tokens[st.trow] = D.tok;
-      if (P.resid_mass) P.resid_mass[b] = R / st.st;
+      if (P.resid_mass) P.resid_mass[b] = R / norm;
     }
   } else {
     // Empty residual after rounding: fall back to a draw from p_j.
     Stop sp = st;
     sp.mode = kModeBonus;
     double tot;
-    const int32_t tok = draw_from_row<DT, NT>(tr, P.V, sp, u, D.shd, D.shi, tot);
+    const int32_t tok = draw_from_row<DT, NT>(row_ptr<DT>(P.target, st.trow, P.V), P.V, sp, u,
+                                              D.shd, D.shi, tot);
     if (tok >= 0) D.tok = tok;
     __syncthreads();
-    if (tid == 0) {
+    if (threadIdx.x == 0) {
       P.out_tokens[st.trow] = D.tok;
       if (P.resid_mass) P.resid_mass[b] = tot / st.st;
     }
