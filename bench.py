@@ -19,6 +19,7 @@ import hashlib
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 from pathlib import Path
@@ -151,30 +152,179 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "dispatches": 5}), flush=True)
 
 
-def cpu_baseline(w, target_seconds: float):
-    """The oracle, as it stands, on the benchmark workload, timed on this host's cores: full
-    passes over the first n requests (n sized for about ``target_seconds``), repeated while
-    the total stays under that time when the whole workload takes less."""
+def cpu_model() -> str:
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, target_seconds: float, runs: int = 3):
+    """The oracle, as it stands, on the benchmark workload, timed on this host's cores: the
+    median of ``runs`` timed runs, each full passes over the first n requests (n sized so that
+    all runs together take about ``target_seconds``)."""
     import oracle
     threads = oracle.max_threads()
     probe_n = min(w.B, 16)
     t = time.perf_counter()
     oracle.verify(w, requests=list(range(probe_n)), threads=threads)
     dt = time.perf_counter() - t
-    n = int(min(w.B, max(probe_n, probe_n * target_seconds / max(dt, 1e-3))))
+    per_run = target_seconds / runs
+    n = int(min(w.B, max(probe_n, probe_n * per_run / max(dt, 1e-3))))
     reqs = list(range(n))
-    passes = 0
-    t = time.perf_counter()
-    while True:
-        oracle.verify(w, requests=reqs, threads=threads)
-        passes += 1
-        dt = time.perf_counter() - t
-        if dt * (passes + 1) / passes > target_seconds or passes >= 100:
-            break
-    positions = int(w.gammas[:n].sum()) * passes
-    return {"value": positions / dt, "unit": "positions/s", "cores": threads, "kind": "oracle",
-            "sample": f"{passes} pass(es) over the first {n} of {w.B} requests of the benchmark "
-                      f"workload ({positions} positions, {dt:.1f} s)"}
+    rates, passes_done = [], []
+    for _ in range(runs):
+        passes = 0
+        t = time.perf_counter()
+        while True:
+            oracle.verify(w, requests=reqs, threads=threads)
+            passes += 1
+            el = time.perf_counter() - t
+            if el * (passes + 1) / passes > per_run or passes >= 100:
+                break
+        rates.append(int(w.gammas[:n].sum()) * passes / el)
+        passes_done.append(passes)
+    return {"value": float(np.median(rates)), "unit": "positions/s", "cores": threads,
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "runs_positions_per_s": [round(r, 1) for r in rates],
+            "sample": f"median of {runs} runs, each {min(passes_done)}-{max(passes_done)} full "
+                      f"pass(es) over the first {n} of {w.B} requests of the benchmark workload "
+                      f"({int(w.gammas[:n].sum())} positions per pass, ~{per_run:.0f} s per run)"}
+
+
+class Measured:
+    """One workload measured on the GPU with the protocol below; holds its device inputs."""
+
+
+def measure(sv, w, workload_id, args, path) -> Measured:
+    """Warm-up, timed region A (step time, nothing on the stream but the library's kernels)
+    and timed region B (per-kernel durations from events the kernels' dispatches record) for
+    workload ``w``: every step is one call over the whole batch, rotating over enough input
+    copies that no step reads cache-hot logits."""
+    import torch
+    m = Measured()
+    m.w, m.workload_id = w, workload_id
+    m.nbytes = w.compulsory_bytes
+    copies = max(2, math.ceil(2 * MALL_BYTES / m.nbytes) + 1)
+    m.copies = min(copies, max(2, (8 << 30) // max(m.nbytes, 1)))
+    base = workloads_mod().to_torch(w)
+    m.inputs = [base] + [dict(base, target=base["target"].clone(), draft=base["draft"].clone())
+                         for _ in range(m.copies - 1)]
+    m.code = sv.SPEC_F32 if w.dtype == "f32" else sv.SPEC_BF16
+    m.ws = sv.alloc_workspace(w.B, w.gamma, w.V, m.code)
+    m.out = torch.empty(w.R_t, dtype=torch.int32, device="cuda")
+    m.nacc = torch.empty(w.B, dtype=torch.int32, device="cuda")
+    hip = HipEvents()
+    m.all_greedy = bool((w.temperatures == 0).all())  # the greedy entry point's workload
+    inputs, out, nacc, ws, copies = m.inputs, m.out, m.nacc, m.ws, m.copies
+
+    def step(k, probe):
+        probe = probe if probe is not None or path == 0 else sv.make_probe(path=path)
+        d = inputs[k % copies]
+        if m.all_greedy:
+            sv.spec_verify_greedy(d["target"], d["tokens"], w.gamma, out, nacc, ws,
+                                  cu_draft=d["cu"], probe=probe)
+        else:
+            sv.spec_verify_sample(d["target"], d["draft"], d["tokens"], d["uniforms"],
+                                  d["temps"], w.gamma, out, nacc, ws, cu_draft=d["cu"],
+                                  probe=probe)
+
+    # Warm-up: the requested W steps, continued until at least 0.25 s of sustained load has
+    # passed (the GPU's clocks settle some milliseconds into a run).
+    warm = 0
+    t_w = time.perf_counter()
+    while warm < args.warmup or time.perf_counter() - t_w < WARMUP_SECONDS:
+        step(warm, None)
+        warm += 1
+        if warm % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    m.warmup_steps_run = warm
+
+    # Timed region A: the step time, with nothing on the stream but the library's kernels
+    # (on this stack every recorded event leaves the GPU idle for several microseconds), and
+    # each input copy's call marshalled once, as a serving loop would hold it.
+    ctl = sv.make_probe(path=path) if path else None
+    if m.all_greedy:
+        calls = [sv.prepare_greedy(d["target"], d["tokens"], w.gamma, out, nacc, ws,
+                                   cu_draft=d["cu"], probe=ctl) for d in inputs]
+    else:
+        calls = [sv.prepare_sample(d["target"], d["draft"], d["tokens"], d["uniforms"],
+                                   d["temps"], w.gamma, out, nacc, ws, cu_draft=d["cu"], probe=ctl)
+                 for d in inputs]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        calls[k % copies]()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    m.ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # Which launch path the calls took: the second launch's events are recorded only by
+    # the two-launch path.
+    evs = hip.create(4)
+    step(0, sv.make_probe(events=evs, path=path))
+    torch.cuda.synchronize()
+    try:
+        hip.elapsed_ms(evs[2], evs[3])
+        m.taken = "two"
+    except RuntimeError:
+        hip.hip.hipGetLastError()
+        m.taken = "one"
+    hip.destroy(evs)
+    m.kernels = KERNELS["one_greedy" if m.taken == "one" and m.all_greedy else m.taken]
+
+    # Timed region B: the same steps again with per-kernel durations from events that each
+    # kernel's dispatch records (probe events) on the stream it runs on.
+    n_ev = 2 * len(m.kernels)
+    evs = hip.create(n_ev * args.steps)
+    probes = [sv.make_probe(events=evs[n_ev * k: n_ev * (k + 1)], path=path)
+              for k in range(args.steps)]
+    for k in range(args.steps):
+        step(k, probes[k])
+    torch.cuda.synchronize()
+    m.per_kernel = {name: np.array([1e3 * hip.elapsed_ms(evs[n_ev * k + 2 * i],
+                                                         evs[n_ev * k + 2 * i + 1])
+                                    for k in range(args.steps)])
+                    for i, name in enumerate(m.kernels)}
+    hip.destroy(evs)
+    m.per_kernel_us = {name: round(float(d.mean()), 2) for name, d in m.per_kernel.items()}
+    m.step_kernels = sum(m.per_kernel.values())  # per step: the call's kernels back to back
+    # the dominant kernel: the row-statistics stream, or the one launch that does everything
+    m.rs_all = m.per_kernel[m.kernels[0]]
+    m.rs_us = float(m.rs_all.mean())
+    m.achieved = m.nbytes / (m.rs_us * 1e-6) / 1e9
+    m.logit_gbps = m.nbytes / (m.ms_per_step * 1e-3) / 1e9
+    return m
+
+
+def workloads_mod():
+    import workloads
+    return workloads
+
+
+def config_entry(m: Measured) -> dict:
+    """A workload's figures for the per-config part of the line (same protocol as the main
+    line; the 70%-of-peak bar is stated per call)."""
+    w = m.w
+    frac = m.logit_gbps / HBM_PEAK_GBPS
+    return {"workload": f"{m.workload_id}: {w.name}", "B": w.B, "gamma_max": w.gamma, "V": w.V,
+            "logit_dtype": w.dtype, "logit_bytes_per_step": m.nbytes,
+            "entry_point": "spec_verify_greedy" if m.all_greedy else "spec_verify_sample",
+            "launch_path": m.taken, "us_per_step": round(m.ms_per_step * 1e3, 2),
+            "positions_per_s": round(w.positions / (m.ms_per_step * 1e-3), 1),
+            "logit_GB_per_s": round(m.logit_gbps, 1), "hbm_frac": round(frac, 4),
+            "meets_70pct_of_peak": bool(frac >= 0.70),
+            "kernel_us": m.per_kernel_us,
+            "dominant_kernel": m.kernels[0],
+            "dominant_kernel_frac": round(m.achieved / HBM_PEAK_GBPS, 4),
+            "k_finish_us": m.per_kernel_us.get("k_finish"),
+            "dominant_kernel_traffic": (lambda r: None if r is None else r["hbm_bytes_per_launch"])(
+                traffic_for_current_kernel(m.kernels[0], m.workload_id)),
+            "step_kernel_us_p10_p50_p90": [round(float(np.percentile(m.step_kernels, q)), 1)
+                                           for q in (10, 50, 90)]}
 
 
 def main():
@@ -184,6 +334,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD,
                     help="1..5; the JSON line is for workload 5 by default")
+    ap.add_argument("--configs", default="1,2,3,4",
+                    help="the other workloads measured in the same run with the same protocol "
+                         "(comma list, or 'none'); reported under 'configs'")
+    ap.add_argument("--config-entry", action="store_true",
+                    help="print only this workload's entry of 'configs' (how the main run "
+                         "measures each of them, in a process of its own)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -224,107 +380,22 @@ def main():
         w = workloads.config(args.workload)
     print(f"[bench] generated workload {args.workload} in {time.perf_counter() - t_gen:.1f} s",
           file=sys.stderr, flush=True)
-    nbytes = w.compulsory_bytes
-    copies = max(2, math.ceil(2 * MALL_BYTES / nbytes) + 1)
-    copies = min(copies, max(2, (8 << 30) // max(nbytes, 1)))
-    base = workloads.to_torch(w)
-    inputs = [base] + [dict(base, target=base["target"].clone(), draft=base["draft"].clone())
-                       for _ in range(copies - 1)]
-    code = sv.SPEC_F32 if w.dtype == "f32" else sv.SPEC_BF16
-    ws = sv.alloc_workspace(w.B, w.gamma, w.V, code)
-    out = torch.empty(w.R_t, dtype=torch.int32, device="cuda")
-    nacc = torch.empty(w.B, dtype=torch.int32, device="cuda")
-    hip = HipEvents()
     path = PATHS[args.path]
-
-    all_greedy = bool((w.temperatures == 0).all())  # the greedy entry point's workload
-
-    def step(k, probe):
-        probe = probe if probe is not None or path == 0 else sv.make_probe(path=path)
-        d = inputs[k % copies]
-        if all_greedy:
-            sv.spec_verify_greedy(d["target"], d["tokens"], w.gamma, out, nacc, ws,
-                                  cu_draft=d["cu"], probe=probe)
-        else:
-            sv.spec_verify_sample(d["target"], d["draft"], d["tokens"], d["uniforms"],
-                                  d["temps"], w.gamma, out, nacc, ws, cu_draft=d["cu"],
-                                  probe=probe)
-
-    # Warm-up: W steps, continued until at least 0.25 s of sustained load has passed (the
-    # GPU's clocks settle some milliseconds into a run).
-    warm = 0
-    t_w = time.perf_counter()
-    while warm < args.warmup or time.perf_counter() - t_w < WARMUP_SECONDS:
-        step(warm, None)
-        warm += 1
-        if warm % 8 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-
-    # Timed region A: the step time, with nothing on the stream but the library's kernels
-    # (on this stack every recorded event leaves the GPU idle for several microseconds), and
-    # each input copy's call marshalled once, as a serving loop would hold it.
-    ctl = sv.make_probe(path=path) if path else None
-    if all_greedy:
-        calls = [sv.prepare_greedy(d["target"], d["tokens"], w.gamma, out, nacc, ws,
-                                   cu_draft=d["cu"], probe=ctl) for d in inputs]
-    else:
-        calls = [sv.prepare_sample(d["target"], d["draft"], d["tokens"], d["uniforms"],
-                                   d["temps"], w.gamma, out, nacc, ws, cu_draft=d["cu"], probe=ctl)
-                 for d in inputs]
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        calls[k % copies]()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-
-    # Which launch path the calls took: the second launch's events are recorded only by
-    # the two-launch path.
-    evs = hip.create(4)
-    step(0, sv.make_probe(events=evs, path=path))
-    torch.cuda.synchronize()
-    try:
-        hip.elapsed_ms(evs[2], evs[3])
-        taken = "two"
-    except RuntimeError:
-        hip.hip.hipGetLastError()
-        taken = "one"
-    hip.destroy(evs)
-    kernels = KERNELS["one_greedy" if taken == "one" and all_greedy else taken]
-
-    # Timed region B: the same steps again with per-kernel durations from events that each
-    # kernel's dispatch records (probe events) on the stream it runs on.
-    n_ev = 2 * len(kernels)
-    evs = hip.create(n_ev * args.steps)
-    probes = [sv.make_probe(events=evs[n_ev * k: n_ev * (k + 1)], path=path)
-              for k in range(args.steps)]
-    for k in range(args.steps):
-        step(k, probes[k])
-    torch.cuda.synchronize()
-    per_kernel = {name: np.array([1e3 * hip.elapsed_ms(evs[n_ev * k + 2 * i], evs[n_ev * k + 2 * i + 1])
-                                  for k in range(args.steps)])
-                  for i, name in enumerate(kernels)}
-    hip.destroy(evs)
-    per_kernel_us = {name: round(float(d.mean()), 2) for name, d in per_kernel.items()}
-    step_kernels = sum(per_kernel.values())  # per step: the call's kernels back to back
-    # the dominant kernel: the row-statistics stream, or the one launch that does everything
-    rs_all = per_kernel[kernels[0]]
-    rs_us = float(rs_all.mean())
-
-    achieved = nbytes / (rs_us * 1e-6) / 1e9
-    traffic = traffic_for_current_kernel(kernels[0], args.workload)
-    positions = w.positions
-    value = positions / (ms_per_step * 1e-3)
-    logit_gbps = nbytes / (ms_per_step * 1e-3) / 1e9
+    m = measure(sv, w, args.workload, args, path)
+    if args.config_entry:  # a child of the main run: this workload's figures only
+        print(json.dumps(config_entry(m)), flush=True)
+        return
+    traffic = traffic_for_current_kernel(m.kernels[0], args.workload)
+    value = w.positions / (m.ms_per_step * 1e-3)
     result = {
         "metric": "verified positions/sec and logit GB/s (fraction of HBM peak), 1 MI355X",
         "value": round(value, 1),
         "unit": "positions/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": warm,
-        "ms_per_step": round(ms_per_step, 5),
+        "warmup": args.warmup,
+        "warmup_steps_run": m.warmup_steps_run,
+        "ms_per_step": round(m.ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -332,30 +403,46 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {w.name}" if args.workload else w.name,
                    "B": w.B, "gamma_max": w.gamma,
-                   "V": w.V, "logit_dtype": w.dtype, "positions_per_step": positions,
-                   "logit_bytes_per_step": nbytes, "input_copies": copies,
-                   "entry_point": "spec_verify_greedy" if all_greedy else "spec_verify_sample",
-                   "launch_path": taken, "parallelism": "single GPU"},
-        "logit_GB_per_s": round(logit_gbps, 1),
-        "hbm_frac": round(logit_gbps / HBM_PEAK_GBPS, 4),
-        "kernel_us": per_kernel_us,
-        "step_kernel_us_p10_p50_p90": [round(float(np.percentile(step_kernels, q)), 1)
+                   "V": w.V, "logit_dtype": w.dtype, "positions_per_step": w.positions,
+                   "logit_bytes_per_step": m.nbytes, "input_copies": m.copies,
+                   "entry_point": "spec_verify_greedy" if m.all_greedy else "spec_verify_sample",
+                   "launch_path": m.taken, "parallelism": "single GPU"},
+        "logit_GB_per_s": round(m.logit_gbps, 1),
+        "hbm_frac": round(m.logit_gbps / HBM_PEAK_GBPS, 4),
+        "kernel_us": m.per_kernel_us,
+        "step_kernel_us_p10_p50_p90": [round(float(np.percentile(m.step_kernels, q)), 1)
                                        for q in (10, 50, 90)],
-        "roofline": {"bound": "hbm", "kernel": kernels[0], "kernel_us": round(rs_us, 2),
-                     "kernel_us_p10_p50_p90": [round(float(np.percentile(rs_all, q)), 1)
+        "roofline": {"bound": "hbm", "kernel": m.kernels[0], "kernel_us": round(m.rs_us, 2),
+                     "kernel_us_p10_p50_p90": [round(float(np.percentile(m.rs_all, q)), 1)
                                                for q in (10, 50, 90)],
-                     "achieved": round(achieved, 1),
+                     "achieved": round(m.achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "frac": round(m.achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else traffic["hbm_bytes_per_launch"]},
         "cpu_baseline": None,
     }
-    result["context"] = context_figures()
-    result["commit"] = time_commit(sv, w, out, nacc, d=inputs[0], steps=args.steps)
-    result["ngram"] = time_ngram(sv, steps=args.steps)
+    result["commit"] = time_commit(sv, w, m.out, m.nacc, d=m.inputs[0], steps=args.steps)
     if args.streams > 1:
-        result["independent_batches"] = time_streams(sv, w, inputs, code, path, all_greedy,
-                                                      args.streams, args.steps)
+        result["independent_batches"] = time_streams(sv, w, m.inputs, m.code, path,
+                                                      m.all_greedy, args.streams, args.steps)
+    # The other workloads, each measured with the same protocol in a child process of its
+    # own: inside one process, inputs allocated after another workload's streamed up to ~5%
+    # slower (workload 4's k_rowstats 394 us after workload 5, 377 us first), so every
+    # workload gets a process whose first allocations are its own.
+    others = [] if args.configs == "none" or args.single_draft else \
+        [int(c) for c in args.configs.split(",") if int(c) != args.workload]
+    result["configs"] = {}
+    for cid in others:
+        cmd = [sys.executable, str(ROOT / "bench.py"), "--workload", str(cid), "--steps",
+               str(args.steps), "--warmup", str(args.warmup), "--path", args.path,
+               "--config-entry"]
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+        sys.stderr.write(r.stderr)
+        if r.returncode != 0:
+            raise RuntimeError(f"measuring workload {cid} failed (exit {r.returncode})")
+        result["configs"][str(cid)] = json.loads(r.stdout.strip().splitlines()[-1])
+    result["context"] = context_figures()
+    result["ngram"] = time_ngram(sv, steps=args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
