@@ -70,7 +70,9 @@ enum {
   SPEC_ERR_DTYPE = -3,      /* dtype is not a spec_dtype                                 */
   SPEC_ERR_WORKSPACE = -4,  /* workspace smaller than spec_verify_workspace_size, or not
                                256-byte aligned                                          */
-  SPEC_ERR_HIP = -5         /* a kernel launch failed                                    */
+  SPEC_ERR_HIP = -5,        /* a kernel launch failed                                    */
+  SPEC_ERR_TOO_LARGE = -6   /* spec_verify_sample_static: the call's workspace would exceed
+                               SPEC_STATIC_SCRATCH_BYTES                                 */
 };
 
 /* Largest gamma (drafts per request) the kernels take. */
@@ -244,6 +246,27 @@ int spec_ngram_propose(const int32_t *seq_tokens, int64_t capacity, const int32_
                        int32_t B, int32_t n_min, int32_t n_max, int32_t gamma,
                        int32_t *out_counts, int32_t *out_dense, int32_t *out_cu,
                        int32_t *out_packed, void *stream);
+
+/*
+ * spec_verify_sample_static — spec_verify_sample for callers that cannot allocate: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Arguments,
+ * results and errors as for spec_verify_sample, without the workspace: the call uses a
+ * static device array of SPEC_STATIC_SCRATCH_BYTES (16 MiB) that each device the library
+ * runs on holds from the first such call until the process ends (its address is taken once
+ * per device with hipGetSymbolAddress; no allocation, no memset).  A call whose
+ * spec_verify_workspace_size exceeds it returns SPEC_ERR_TOO_LARGE with nothing enqueued
+ * (workload sizes up to B = 512, gamma = 8, V = 128256 fit).  The array keeps the last
+ * call's contents; what must start at zero (the one-launch counters) is zero at load and
+ * is returned to zero by every call.  All calls on one device share the one array: calls
+ * that overlap on a device (unordered streams, or other host threads) race and must not be
+ * made; calls ordered on one stream are safe.
+ */
+#define SPEC_STATIC_SCRATCH_BYTES (16u << 20)
+int spec_verify_sample_static(const void *target_logits, const void *draft_logits, int dtype,
+                              const int32_t *draft_tokens, const float *uniforms,
+                              const float *temperatures, int32_t B, int32_t gamma,
+                              const int32_t *cu_draft, int64_t V, int32_t *out_tokens,
+                              int32_t *out_num_accepted, const spec_probe *probe, void *stream);
 
 /* Workspace bytes needed by either entry point for these sizes; 0 for invalid sizes. */
 size_t spec_verify_workspace_size(int32_t B, int32_t gamma, int64_t V, int dtype);

@@ -19,6 +19,9 @@ SPEC_MAX_GAMMA = 64
 SPEC_NGRAM_MAX_N = 64
 SPEC_OK = 0
 SPEC_PATH_AUTO, SPEC_PATH_TWO, SPEC_PATH_ONE = 0, 1, 2
+SPEC_ERR_TOO_LARGE = -6
+# the static scratch of spec_verify_sample_static (per device, for the life of the process)
+SPEC_STATIC_SCRATCH_BYTES = 16 << 20
 # the workspace's leading counter region (2 x 2048 counters, one per 128-byte line), which
 # must be zero before a workspace's first use and which every call leaves at zero
 COUNTER_BYTES = 2 * 2048 * 128
@@ -53,6 +56,9 @@ def lib():
         L.spec_verify_sample.restype = ctypes.c_int
         L.spec_verify_sample.argtypes = [P, P, ctypes.c_int, P, P, P, i32, i32, P, i64, P, P,
                                          P, sz, P, P]
+        L.spec_verify_sample_static.restype = ctypes.c_int
+        L.spec_verify_sample_static.argtypes = [P, P, ctypes.c_int, P, P, P, i32, i32, P, i64,
+                                                P, P, P, P]
         L.spec_verify_greedy.restype = ctypes.c_int
         L.spec_verify_greedy.argtypes = [P, ctypes.c_int, P, i32, i32, P, i64, P, P, P, sz, P,
                                          P]
@@ -157,7 +163,8 @@ def _sample_args(target_logits, draft_logits, draft_tokens, uniforms, temperatur
         _dev(cu_draft, "cu_draft", torch.int32, B + 1), V,
         _dev(out_tokens, "out_tokens", torch.int32),
         _dev(out_num_accepted, "out_num_accepted", torch.int32, B),
-        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _dev(workspace, "workspace"),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
         None if probe is None else ctypes.byref(probe), _stream(stream))
 
 
@@ -186,6 +193,19 @@ def spec_verify_sample(target_logits, draft_logits, draft_tokens, uniforms, temp
     args = _sample_args(target_logits, draft_logits, draft_tokens, uniforms, temperatures,
                         gamma, out_tokens, out_num_accepted, workspace, cu_draft, probe, stream)
     _check(lib().spec_verify_sample(*args), "spec_verify_sample")
+
+
+def spec_verify_sample_static(target_logits, draft_logits, draft_tokens, uniforms,
+                              temperatures, gamma: int, out_tokens, out_num_accepted,
+                              cu_draft=None, probe: Optional[_Probe] = None,
+                              stream=None) -> None:
+    """``spec_verify_sample`` with no workspace argument and no allocation: the library's
+    static per-device scratch (SPEC_STATIC_SCRATCH_BYTES) is used.  Calls that overlap on one
+    device race; calls ordered on one stream are safe."""
+    a = _sample_args(target_logits, draft_logits, draft_tokens, uniforms, temperatures, gamma,
+                     out_tokens, out_num_accepted, None, cu_draft, probe, stream)
+    _check(lib().spec_verify_sample_static(*a[:12], a[14], a[15]),
+           "spec_verify_sample_static")
 
 
 def spec_verify_greedy(target_logits, draft_tokens, gamma: int, out_tokens,

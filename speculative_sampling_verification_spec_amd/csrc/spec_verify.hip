@@ -55,6 +55,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
@@ -1974,6 +1975,35 @@ int dispatch(const Params &P, const Plan &pl, const spec_probe *probe, hipStream
   return vec ? run<DT, true>(P, pl, probe, s) : run<DT, false>(P, pl, probe, s);
 }
 
+// ------------------------------------------------------------------ the static scratch
+
+// The allocation-free entry point's workspace: one array per device, in the code object's
+// zero-initialised device data, kept until the process ends.  Zero at load, which is what the
+// one-launch counters at its start need, and every call returns them to zero.  Host code never
+// passes `scratch` itself (on the host its name is a stand-in, not a device address): it uses
+// the address hipGetSymbolAddress gives for the current device, fetched once per device.
+static __device__ __align__(256) unsigned char scratch[SPEC_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_addr[kMaxDevices];
+
+// The current device's address of `scratch` (nullptr if it cannot be had).
+void *scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  void *ptr = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  g_scratch_addr[dev].store(ptr, std::memory_order_release);  // the same value for any racer
+  return ptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1994,6 +2024,9 @@ const char *spec_verify_strerror(int code) {
     case SPEC_ERR_DTYPE: return "dtype is neither SPEC_F32 nor SPEC_BF16";
     case SPEC_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
     case SPEC_ERR_HIP: return "HIP kernel launch failed";
+    case SPEC_ERR_TOO_LARGE:
+      return "the call needs more scratch than the static buffer holds "
+             "(SPEC_STATIC_SCRATCH_BYTES; spec_verify_workspace_size gives the need)";
     default: return "unknown spec_verify error code";
   }
 }
@@ -2039,6 +2072,27 @@ int spec_verify_sample(const void *target_logits, const void *draft_logits, int 
   hipStream_t s = static_cast<hipStream_t>(stream);
   return dtype == SPEC_F32 ? dispatch<SPEC_F32>(P, pl, probe, s, vec)
                            : dispatch<SPEC_BF16>(P, pl, probe, s, vec);
+}
+
+int spec_verify_sample_static(const void *target_logits, const void *draft_logits, int dtype,
+                              const int32_t *draft_tokens, const float *uniforms,
+                              const float *temperatures, int32_t B, int32_t gamma,
+                              const int32_t *cu_draft, int64_t V, int32_t *out_tokens,
+                              int32_t *out_num_accepted, const spec_probe *probe,
+                              void *stream) {
+  SPEC_TRY(check_shape(B, gamma, V, dtype));
+  if (B == 0) return SPEC_OK;
+  if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !temperatures ||
+      !out_tokens || !out_num_accepted)
+    return SPEC_ERR_NULL;
+  const size_t need = spec_verify_workspace_size(B, gamma, V, dtype);
+  if (need == 0) return SPEC_ERR_SHAPE;
+  if (need > SPEC_STATIC_SCRATCH_BYTES) return SPEC_ERR_TOO_LARGE;
+  void *ws = scratch_address();
+  if (!ws) return SPEC_ERR_HIP;
+  return spec_verify_sample(target_logits, draft_logits, dtype, draft_tokens, uniforms,
+                            temperatures, B, gamma, cu_draft, V, out_tokens, out_num_accepted, ws,
+                            SPEC_STATIC_SCRATCH_BYTES, probe, stream);
 }
 
 int spec_verify_greedy(const void *target_logits, int dtype, const int32_t *draft_tokens,

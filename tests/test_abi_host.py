@@ -23,7 +23,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert names == ["spec_ngram_propose", "spec_verify_commit", "spec_verify_greedy",
-                     "spec_verify_sample", "spec_verify_strerror", "spec_verify_workspace_size"]
+                     "spec_verify_sample", "spec_verify_sample_static", "spec_verify_strerror",
+                     "spec_verify_workspace_size"]
     lib = sv.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -36,7 +37,7 @@ def test_workspace_size_and_strerror():
     assert sv.spec_verify_workspace_size(1, 4, 0, sv.SPEC_F32) == 0
     assert sv.spec_verify_workspace_size(1, 4, 100, 7) == 0
     assert sv.spec_verify_workspace_size(-1, 4, 100, 0) == 0
-    for code in (0, -1, -2, -3, -4, -5, -99):
+    for code in (0, -1, -2, -3, -4, -5, -6, -99):
         assert isinstance(sv.spec_verify_strerror(code), str)
     assert "NULL" in sv.spec_verify_strerror(-1)
 
@@ -182,3 +183,30 @@ def test_probe_struct_matches_the_header(tmp_path):
                                           text=True).stdout.split()]
     assert got[0] == ctypes.sizeof(sv._Probe)
     assert got[1:] == [getattr(sv._Probe, f).offset for f in fields]
+
+
+def _static(**kw):
+    a = dict(t=FAKE, d=FAKE, dtype=1, tok=FAKE, u=FAKE, temp=FAKE, B=2, gamma=3, cu=None,
+             V=1000, out=FAKE, n=FAKE, probe=None, stream=None)
+    a.update(kw)
+    return sv.lib().spec_verify_sample_static(a["t"], a["d"], a["dtype"], a["tok"], a["u"],
+                                              a["temp"], a["B"], a["gamma"], a["cu"], a["V"],
+                                              a["out"], a["n"], a["probe"], a["stream"])
+
+
+@pytest.mark.parametrize("field", ["t", "d", "tok", "u", "temp", "out", "n"])
+def test_static_entry_point_rejects_null_pointers(field):
+    assert _static(**{field: None}) == -1
+
+
+def test_static_entry_point_refuses_calls_beyond_its_scratch():
+    # the size check comes before anything touches the device
+    assert sv.spec_verify_workspace_size(512, 8, 128256, sv.SPEC_BF16) \
+        <= sv.SPEC_STATIC_SCRATCH_BYTES
+    big = dict(B=4096, gamma=8, V=128256)
+    assert sv.spec_verify_workspace_size(4096, 8, 128256, sv.SPEC_BF16) \
+        > sv.SPEC_STATIC_SCRATCH_BYTES
+    assert _static(**big) == sv.SPEC_ERR_TOO_LARGE
+    assert "SPEC_STATIC_SCRATCH_BYTES" in sv.spec_verify_strerror(sv.SPEC_ERR_TOO_LARGE)
+    assert _static(B=2, gamma=65) == -2 and _static(dtype=9) == -3
+    assert _static(B=0, t=None) == 0

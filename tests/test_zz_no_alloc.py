@@ -1,0 +1,71 @@
+"""The allocation-free entry point (spec_verify_sample_static, static per-device scratch)
+against the workspace entry point (spec_verify_sample) and the oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle
+import speculative_sampling_verification_spec_amd as sv
+import workloads
+from tests import parity
+from tests.gpu_run import run, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _static_run(w, path):
+    import torch
+    d = to_device(w)
+    f64 = dict(dtype=torch.float64, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    t = dict(p_x=torch.full((w.R_d,), np.nan, **f64), q_x=torch.full((w.R_d,), np.nan, **f64),
+             row_max_t=torch.full((w.R_t,), np.nan, **f32),
+             row_sum_t=torch.full((w.R_t,), np.nan, **f64),
+             row_max_d=torch.full((w.R_d,), np.nan, **f32),
+             row_sum_d=torch.full((w.R_d,), np.nan, **f64),
+             resid_mass=torch.full((w.B,), np.nan, **f64))
+    out = torch.full((w.R_t,), -7, dtype=torch.int32, device="cuda")
+    nacc = torch.full((w.B,), -7, dtype=torch.int32, device="cuda")
+    sv.spec_verify_sample_static(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temps"],
+                                 w.gamma, out, nacc, cu_draft=d["cu"],
+                                 probe=sv.make_probe(**t, path=path))
+    torch.cuda.synchronize()
+    res = dict(out_tokens=out.cpu().numpy(), num_accepted=nacc.cpu().numpy())
+    res.update({k: v.cpu().numpy() for k, v in t.items()})
+    return res
+
+
+@pytest.mark.parametrize("path", [sv.SPEC_PATH_AUTO, sv.SPEC_PATH_TWO, sv.SPEC_PATH_ONE])
+def test_static_scratch_calls_match_the_workspace_entry_point(path):
+    # two calls in a row on the static scratch, the second smaller (and of the other dtype):
+    # every output and probe equals the workspace entry point's on the same inputs, and both
+    # meet the parity rules against the oracle
+    cases = [dict(B=40, gamma=5, V=30000, dtype="bf16", seed=501),
+             dict(B=7, gamma=3, V=5000, dtype="f32", seed=502)]
+    for kw in cases:
+        temps = np.where(np.arange(kw["B"]) % 4 == 1, 0.0, np.linspace(0.4, 1.4, kw["B"]))
+        w = workloads.small(**kw, ragged=True, temperatures=temps, draft_sigma=0.8)
+        print(f"[gpu] static scratch B={w.B} gamma={w.gamma} V={w.V} {w.dtype} path={path}",
+              flush=True)
+        got = _static_run(w, path)
+        ref = run(w, path=path)
+        for k in ref:
+            np.testing.assert_array_equal(got[k], ref[k], err_msg=k)
+        parity.compare(w, got, oracle.verify(w))
+
+
+def test_static_scratch_refuses_a_call_beyond_its_size():
+    import torch
+    w = workloads.small(B=2, gamma=1, V=64, dtype="bf16", seed=503)
+    d = to_device(w)
+    out = torch.full((4096 * 9,), -7, dtype=torch.int32, device="cuda")
+    nacc = torch.full((4096,), -7, dtype=torch.int32, device="cuda")
+    big = torch.zeros((4096 * 9, 128256), dtype=torch.bfloat16, device="cuda")
+    temps = torch.ones(4096, dtype=torch.float32, device="cuda")
+    tok = torch.zeros(4096 * 8, dtype=torch.int32, device="cuda")
+    uni = torch.zeros((4096 * 9, 2), dtype=torch.float32, device="cuda")
+    with pytest.raises(sv.SpecVerifyError) as e:
+        sv.spec_verify_sample_static(big, big, tok, uni, temps, 8, out, nacc)
+    assert e.value.code == sv.SPEC_ERR_TOO_LARGE
+    torch.cuda.synchronize()
+    assert (out.cpu().numpy() == -7).all() and (nacc.cpu().numpy() == -7).all()
+    del d
