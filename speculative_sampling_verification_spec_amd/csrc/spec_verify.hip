@@ -335,6 +335,36 @@ __device__ __forceinline__ float unit_sum(const float (&e)[W]) {
 // or invalidate.  The writer waits for its stores to complete before it updates an arrival
 // counter (a device-scope atomic add); a reader loads them only after its own update of that
 // counter has returned the count that makes it the last arrival.
+//
+// ORDERING ASSUMPTION.  Every hand-off inside a launch uses this protocol and no release or
+// acquire fence:
+//   writer: relaxed agent-scope atomic stores of the data
+//           -> wait_memory() (s_waitcnt 0: every store acknowledged by the device-coherent
+//              level; compiler signal fences on both sides keep the compiler from moving
+//              memory operations across it)
+//           -> __syncthreads() (all of the workgroup's writers have waited)
+//           -> one relaxed agent-scope atomic add on the request's counter;
+//   reader: its own relaxed atomic on that counter returns the value that makes it the last
+//           (or its poll sees the final count) -> __syncthreads() -> relaxed agent-scope
+//           atomic loads of the data.
+// The HIP memory model gives relaxed atomics no such ordering; the protocol relies on gfx950
+// completing a store before acknowledging it and on agent-scope accesses bypassing the
+// non-coherent L2, so that an acknowledged store is seen by any later agent-scope load.
+// Fences were left out on purpose: on gfx950 an agent-scope release / acquire is a full L2
+// writeback / invalidate, measured at ~60 ns of serialised GPU time each, which one fence
+// pair per row tile turned into a 12.7x slower stream.  The protocol was run in soak tests
+// with the partials poisoned between runs (no wrong or missing merge, counters back to zero).
+// The sites that rely on it:
+//   - share_store / share_load: the stop rows' chunk sums (stream_chunks -> draw_pick), in
+//     k_finish (counter `done`), k_onepass (completion counter) and the accurate redraw (the
+//     drawing workgroup reads back its own sums, the same protocol within one workgroup);
+//   - put_partial / get_partial and put_u32 / get_rec with SHARED: the row partials and slot
+//     records that k_greedy1 and k_onepass hand to the request's last arrival or its waiting
+//     tiles (counter `arrive`, the 64-bit arrival word of k_onepass);
+//   - the counters' own resets by their last user (k_greedy1, k_onepass), which the next
+//     launch reads after the kernel boundary.
+// Between two launches (k_rowstats -> k_finish) the kernel boundary orders everything and
+// plain accesses suffice.
 __device__ __forceinline__ void share_store(double *p, double v) {
   __hip_atomic_store(reinterpret_cast<unsigned long long *>(p),
                      (unsigned long long)__double_as_longlong(v), __ATOMIC_RELAXED,
