@@ -140,6 +140,48 @@ def context_figures():
             "read_stream_frac": round(gbps / HBM_PEAK_GBPS, 4), "read_stream_bytes": nbytes}
 
 
+def read_reference_us(nbytes: int) -> float:
+    """GPU time of one plain read stream (libspecbench.so's 16-byte nontemporal reads, 64 KB per
+    workgroup) over ``nbytes``, the reads rotating over enough buffers (> 2 x the last-level
+    cache) that none is cache-hot: the minimum over three trials of the mean per read."""
+    import torch
+    L = ctypes.CDLL(str(ROOT / "speculative_sampling_verification_spec_amd" / "libspecbench.so"))
+    L.spec_bench_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nbytes = max(16, nbytes // 16 * 16)
+    nbuf = max(3, math.ceil(2 * MALL_BYTES / nbytes) + 1)
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    reps = max(nbuf, 30)
+
+    def run(n):
+        for i in range(n):
+            if L.spec_bench_read(ctypes.c_void_p(bufs[i % nbuf].data_ptr()), nbytes,
+                                 ctypes.c_void_p(sink.data_ptr()), stream) != 0:
+                raise RuntimeError("reference read launch failed")
+
+    run(reps)
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(3):
+        t0 = time.perf_counter()
+        run(reps)
+        torch.cuda.synchronize()
+        best = min(best, (time.perf_counter() - t0) * 1e6 / reps)
+    del bufs
+    return best
+
+
+def stop_row_bytes(w, nacc) -> int:
+    """Bytes of the stop rows a call re-reads: two rows (target and draft) per sampled request
+    that rejected a draft, one (the target's bonus row) per sampled request that accepted all."""
+    es = 4 if w.dtype == "f32" else 2
+    rows = sum(2 if int(nacc[b]) < int(w.gammas[b]) else 1
+               for b in range(w.B) if w.temperatures[b] > 0)
+    return rows * w.V * es
+
+
 def copy_calibration():
     """A plain device-to-device copy of COPY_BYTES, the reference the HBM byte counters
     (FETCH_SIZE, WRITE_SIZE) are scaled by."""
@@ -297,7 +339,21 @@ def measure(sv, w, workload_id, args, path) -> Measured:
     m.rs_us = float(m.rs_all.mean())
     m.achieved = m.nbytes / (m.rs_us * 1e-6) / 1e9
     m.logit_gbps = m.nbytes / (m.ms_per_step * 1e-3) / 1e9
+    m.stop_bytes = stop_row_bytes(w, m.nacc.cpu().numpy())
     return m
+
+
+def read_floors(m: Measured) -> dict:
+    """The plain read-stream reference at this workload's sizes, beside its step: the time to
+    read its compulsory logit bytes once, and its stop rows once, and what two launches that
+    did nothing but those two reads (plus one back-to-back launch) would reach."""
+    t_logits = read_reference_us(m.nbytes)
+    t_stop = read_reference_us(m.stop_bytes) if m.stop_bytes else 0.0
+    t_launch = 1.3  # one empty launch back to back on this stack (context.empty_launch_us)
+    floor = t_logits + t_stop + (t_launch if m.taken == "two" else 0.0)
+    return {"read_logit_bytes_us": round(t_logits, 2), "stop_row_bytes": m.stop_bytes,
+            "read_stop_row_bytes_us": round(t_stop, 2),
+            "reads_only_frac": round(m.nbytes / (floor * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
 def workloads_mod():
@@ -324,7 +380,8 @@ def config_entry(m: Measured) -> dict:
             "dominant_kernel_traffic": (lambda r: None if r is None else r["hbm_bytes_per_launch"])(
                 traffic_for_current_kernel(m.kernels[0], m.workload_id)),
             "step_kernel_us_p10_p50_p90": [round(float(np.percentile(m.step_kernels, q)), 1)
-                                           for q in (10, 50, 90)]}
+                                           for q in (10, 50, 90)],
+            "read_reference": read_floors(m)}
 
 
 def main():
@@ -420,6 +477,7 @@ def main():
                      "frac": round(m.achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else traffic["hbm_bytes_per_launch"]},
         "cpu_baseline": None,
+        "read_reference": read_floors(m),
     }
     result["commit"] = time_commit(sv, w, m.out, m.nacc, d=m.inputs[0], steps=args.steps)
     if args.streams > 1:
