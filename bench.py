@@ -38,6 +38,7 @@ KERNELS = {"two": ["k_rowstats", "k_finish"], "one_greedy": ["k_greedy1"],
 PATHS = {"auto": 0, "two": 1, "one": 2}
 DEFAULT_WORKLOAD = 5
 WARMUP_SECONDS = 0.25
+STEP_REPEATS = 9                # extra repeats of the K-step region, for the step time's spread
 PROFILES = ROOT / "profiles"
 COPY_BYTES = 1 << 30            # plain copy used to calibrate the HBM byte counters
 KERNEL_SRC = ROOT / "speculative_sampling_verification_spec_amd" / "csrc" / "spec_verify.hip"
@@ -303,6 +304,16 @@ def measure(sv, w, workload_id, args, path) -> Measured:
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     m.ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # The same region repeated (not part of the step time above): the spread of the per-step
+    # time over repeats of K steps each.
+    reps = []
+    for _ in range(STEP_REPEATS):
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            calls[k % copies]()
+        torch.cuda.synchronize()
+        reps.append((time.perf_counter() - t0) * 1e6 / args.steps)
+    m.step_us_repeats = reps
 
     # Which launch path the calls took: the second launch's events are recorded only by
     # the two-launch path.
@@ -363,6 +374,10 @@ def read_floors(m: Measured) -> dict:
             "reads_only_frac": round(m.nbytes / (floor * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
+def pct(xs):
+    return [round(float(np.percentile(xs, q)), 2) for q in (10, 50, 90)]
+
+
 def workloads_mod():
     import workloads
     return workloads
@@ -377,6 +392,7 @@ def config_entry(m: Measured) -> dict:
             "logit_dtype": w.dtype, "logit_bytes_per_step": m.nbytes,
             "entry_point": "spec_verify_greedy" if m.all_greedy else "spec_verify_sample",
             "launch_path": m.taken, "us_per_step": round(m.ms_per_step * 1e3, 2),
+            "step_us_p10_p50_p90_over_repeats": pct(m.step_us_repeats),
             "graph_us_per_step": round(m.graph_us_per_step, 2),
             "positions_per_s": round(w.positions / (m.ms_per_step * 1e-3), 1),
             "logit_GB_per_s": round(m.logit_gbps, 1), "hbm_frac": round(frac, 4),
@@ -461,6 +477,7 @@ def main():
         "warmup": args.warmup,
         "warmup_steps_run": m.warmup_steps_run,
         "ms_per_step": round(m.ms_per_step, 5),
+        "step_us_p10_p50_p90_over_repeats": pct(m.step_us_repeats),
         "graph_us_per_step": round(m.graph_us_per_step, 2),
         "higher_is_better": True,
         "scaling": "weak",

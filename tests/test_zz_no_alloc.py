@@ -69,3 +69,60 @@ def test_static_scratch_refuses_a_call_beyond_its_size():
     torch.cuda.synchronize()
     assert (out.cpu().numpy() == -7).all() and (nacc.cpu().numpy() == -7).all()
     del d
+
+
+@pytest.mark.parametrize("path", [sv.SPEC_PATH_TWO, sv.SPEC_PATH_ONE], ids=["two", "one"])
+def test_static_scratch_call_replays_in_a_graph(path):
+    # the callers this entry point is for: a step captured once in a HIP graph, nothing
+    # allocated, replayed with new inputs copied in between replays (and eager calls on the
+    # same scratch in between); every replay equals the eager call on the same inputs
+    import torch
+    B, gamma, V = 24, 4, 32000
+    mixed = np.where(np.arange(B) % 4 == 0, 0.0, 0.9)
+    wl = [workloads.generate(name=f"static-graph{s}", B=B, V=V, dtype="bf16", gammas=[gamma] * B,
+                             dense=True, target_sigma=3.0, draft_sigma=1.0,
+                             temperatures=0.7 if s != 1 else mixed, seed=600 + s)
+          for s in range(3)]
+    print(f"[gpu] static scratch in a graph B={B} gamma={gamma} V={V} path={path}", flush=True)
+    host = [workloads.to_torch(w, "cpu") for w in wl]
+    dev = {k: v.cuda() for k, v in host[0].items() if v is not None}
+    out = torch.empty(wl[0].R_t, dtype=torch.int32, device="cuda")
+    nacc = torch.empty(B, dtype=torch.int32, device="cuda")
+    probe = sv.make_probe(path=path)
+
+    def load(i):
+        for k, v in host[i].items():
+            if v is not None:
+                dev[k].copy_(v)
+        out.fill_(-7)
+        nacc.fill_(-7)
+        torch.cuda.synchronize()
+
+    def call():
+        sv.spec_verify_sample_static(dev["target"], dev["draft"], dev["tokens"], dev["uniforms"],
+                                     dev["temps"], gamma, out, nacc, probe=probe)
+
+    eager = []
+    for i in range(3):
+        load(i)
+        call()
+        torch.cuda.synchronize()
+        eager.append((out.cpu().numpy().copy(), nacc.cpu().numpy().copy()))
+    parity.compare(wl[0], dict(out_tokens=eager[0][0], num_accepted=eager[0][1]),
+                   oracle.verify(wl[0]), probes=False)
+    g = torch.cuda.CUDAGraph()
+    load(0)
+    with torch.cuda.graph(g):  # the eager calls above took the scratch's address
+        call()
+    torch.cuda.synchronize()
+    for rnd, i in enumerate([0, 1, 2, 2, 0, 1]):
+        load(i)
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(out.cpu().numpy(), eager[i][0], err_msg=f"replay {rnd}")
+        np.testing.assert_array_equal(nacc.cpu().numpy(), eager[i][1], err_msg=f"replay {rnd}")
+        if rnd == 2:
+            load(1)
+            call()
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(nacc.cpu().numpy(), eager[1][1])
