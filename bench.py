@@ -354,9 +354,11 @@ def measure(sv, w, workload_id, args, path) -> Measured:
     # it): the same steps captured once in a HIP graph (enough of them for ~2 ms per replay, so
     # the events around a replay weigh little) and replayed, the GPU time per step without the
     # host's per-call cost, which bounds region A for the smallest workloads.
-    n_graph = copies * max(2, math.ceil(2000.0 / max(m.ms_per_step * 1e3, 1.0) / copies))
-    m.graph_us_per_step = graph_us_per_call([(lambda k=k: step(k, None))
-                                             for k in range(n_graph)])
+    m.graph_us_per_step = None
+    if not args.no_graph:
+        n_graph = copies * max(2, math.ceil(2000.0 / max(m.ms_per_step * 1e3, 1.0) / copies))
+        m.graph_us_per_step = graph_us_per_call([(lambda k=k: step(k, None))
+                                                 for k in range(n_graph)])
     m.stop_bytes = stop_row_bytes(w, m.nacc.cpu().numpy())
     return m
 
@@ -372,6 +374,10 @@ def read_floors(m: Measured) -> dict:
     return {"read_logit_bytes_us": round(t_logits, 2), "stop_row_bytes": m.stop_bytes,
             "read_stop_row_bytes_us": round(t_stop, 2),
             "reads_only_frac": round(m.nbytes / (floor * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
+def rnd(x):
+    return None if x is None else round(x, 2)
 
 
 def pct(xs):
@@ -393,7 +399,7 @@ def config_entry(m: Measured) -> dict:
             "entry_point": "spec_verify_greedy" if m.all_greedy else "spec_verify_sample",
             "launch_path": m.taken, "us_per_step": round(m.ms_per_step * 1e3, 2),
             "step_us_p10_p50_p90_over_repeats": pct(m.step_us_repeats),
-            "graph_us_per_step": round(m.graph_us_per_step, 2),
+            "graph_us_per_step": rnd(m.graph_us_per_step),
             "positions_per_s": round(w.positions / (m.ms_per_step * 1e-3), 1),
             "logit_GB_per_s": round(m.logit_gbps, 1), "hbm_frac": round(frac, 4),
             "meets_70pct_of_peak": bool(frac >= 0.70),
@@ -421,6 +427,9 @@ def main():
     ap.add_argument("--config-entry", action="store_true",
                     help="print only this workload's entry of 'configs' (how the main run "
                          "measures each of them, in a process of its own)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-replay timing (profiling runs: the trace then ends with "
+                         "timed region B)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -478,7 +487,7 @@ def main():
         "warmup_steps_run": m.warmup_steps_run,
         "ms_per_step": round(m.ms_per_step, 5),
         "step_us_p10_p50_p90_over_repeats": pct(m.step_us_repeats),
-        "graph_us_per_step": round(m.graph_us_per_step, 2),
+        "graph_us_per_step": rnd(m.graph_us_per_step),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -519,7 +528,7 @@ def main():
     for cid in others:
         cmd = [sys.executable, str(ROOT / "bench.py"), "--workload", str(cid), "--steps",
                str(args.steps), "--warmup", str(args.warmup), "--path", args.path,
-               "--config-entry"]
+               "--config-entry"] + (["--no-graph"] if args.no_graph else [])
         r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
         sys.stderr.write(r.stderr)
         if r.returncode != 0:
