@@ -441,6 +441,11 @@ def main():
                          "each (V = 128256 bf16, T = 0.7)")
     ap.add_argument("--streams", type=int, default=1, metavar="S",
                     help="also time independent batches spread over S streams (context figure)")
+    ap.add_argument("--shard", type=int, default=1, metavar="G",
+                    help="instead of the JSON line: the workload split by requests over G GPUs "
+                         "(ranges balanced by logit bytes), each GPU's share timed on this one "
+                         "GPU in a process of its own; prints the shares and the slowest")
+    ap.add_argument("--shard-index", type=int, default=-1, help=argparse.SUPPRESS)
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -470,10 +475,19 @@ def main():
         w = workloads.config(args.workload)
     print(f"[bench] generated workload {args.workload} in {time.perf_counter() - t_gen:.1f} s",
           file=sys.stderr, flush=True)
+    if args.shard > 1 and args.shard_index < 0:
+        print(json.dumps(time_shards(w, args)), flush=True)
+        return
+    if args.shard_index >= 0:  # a child of time_shards: this GPU's share of the requests
+        lo, hi = workloads.shard_ranges(w, args.shard)[args.shard_index]
+        w = w.requests(lo, hi)
     path = PATHS[args.path]
     m = measure(sv, w, args.workload, args, path)
     if args.config_entry:  # a child of the main run: this workload's figures only
-        print(json.dumps(config_entry(m)), flush=True)
+        e = config_entry(m)
+        if args.shard_index >= 0:  # the counters were taken on the whole workload
+            e["dominant_kernel_traffic"] = None
+        print(json.dumps(e), flush=True)
         return
     traffic = traffic_for_current_kernel(m.kernels[0], args.workload)
     value = w.positions / (m.ms_per_step * 1e-3)
@@ -539,6 +553,34 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def time_shards(w, args) -> dict:
+    """The workload split by requests over G GPUs: each share is the same call over fewer
+    requests, with no communication, so each is timed alone on this GPU (a child process per
+    share, the same protocol as the main line); a G-GPU step lasts as long as its slowest
+    share."""
+    import workloads
+    G = args.shard
+    shares = []
+    for k, (lo, hi) in enumerate(workloads.shard_ranges(w, G)):
+        cmd = [sys.executable, str(ROOT / "bench.py"), "--workload", str(args.workload),
+               "--steps", str(args.steps), "--warmup", str(args.warmup), "--path", args.path,
+               "--shard", str(G), "--shard-index", str(k), "--config-entry", "--no-graph"]
+        print(f"[bench] share {k} of {G}: requests {lo}..{hi - 1}", file=sys.stderr, flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+        sys.stderr.write(r.stderr)
+        if r.returncode != 0:
+            raise RuntimeError(f"measuring share {k} failed (exit {r.returncode})")
+        e = json.loads(r.stdout.strip().splitlines()[-1])
+        e["requests"] = [lo, hi]
+        shares.append(e)
+    slowest = max(s["us_per_step"] for s in shares)
+    return {"workload": f"{args.workload}: {w.name}", "gpus_modelled": G,
+            "split": "by requests, contiguous ranges balanced by logit bytes; no communication",
+            "shares": shares, "step_us_slowest_share": slowest,
+            "positions_per_s_all_gpus": round(w.positions / (slowest * 1e-6), 1),
+            "logit_GB_per_s_all_gpus": round(w.compulsory_bytes / (slowest * 1e-6) / 1e9, 1)}
 
 
 NGRAM = dict(B=512, capacity=8192, n_min=2, n_max=5, gamma=8, seed=77)

@@ -75,3 +75,38 @@ def test_vocabulary_masks_are_shared_by_a_request_and_leave_a_finite_logit():
     w = workloads.small(B=2, gamma=1, V=50, dtype="f32", seed=5, mask_frac=1.0)
     zt = workloads.decode(w.target, "f32")
     assert np.isfinite(zt[:, 0]).all() and np.isinf(zt[:, 1:]).all()
+
+
+@pytest.mark.parametrize("ragged", [False, True])
+def test_a_range_of_requests_verifies_as_the_batch_slice(ragged):
+    # Requests are independent: verifying requests [lo, hi) on their own (the share one GPU
+    # gets when a batch is split by requests) gives exactly the whole batch's results for them.
+    import oracle
+    temps = np.where(np.arange(11) % 3 == 0, 0.0, np.linspace(0.4, 1.3, 11))
+    w = workloads.small(B=11, gamma=5, V=300, dtype="bf16", seed=21, ragged=ragged,
+                        temperatures=temps, draft_sigma=0.8)
+    full = oracle.verify(w)
+    for lo, hi in [(0, 11), (0, 4), (4, 5), (5, 11), (10, 11)]:
+        s = w.requests(lo, hi)
+        assert s.B == hi - lo and s.positions == int(w.gammas[lo:hi].sum())
+        assert s.compulsory_bytes == int(w.request_bytes()[lo:hi].sum())
+        part = oracle.verify(s)
+        t0 = int(w.target_base[lo])
+        np.testing.assert_array_equal(part["num_accepted"], full["num_accepted"][lo:hi])
+        np.testing.assert_array_equal(part["out_tokens"],
+                                      full["out_tokens"][t0:t0 + s.R_t])
+        np.testing.assert_array_equal(part["resid_mass"], full["resid_mass"][lo:hi])
+
+
+def test_shard_ranges_cover_the_batch_and_balance_its_bytes():
+    w = workloads.small(B=40, gamma=8, V=128, dtype="bf16", seed=5, ragged=True,
+                        temperatures=np.where(np.arange(40) % 5 == 0, 0.0, 0.9))
+    rb = w.request_bytes()
+    assert int(rb.sum()) == w.compulsory_bytes
+    for G in (1, 2, 3, 8, 40):
+        r = workloads.shard_ranges(w, G)
+        assert len(r) == G and r[0][0] == 0 and r[-1][1] == w.B
+        assert all(a < b for a, b in r) and all(r[k][1] == r[k + 1][0] for k in range(G - 1))
+        # contiguous ranges cut where the running bytes reach k / G of the total: no range
+        # holds more than its share plus one request
+        assert max(int(rb[a:b].sum()) for a, b in r) <= rb.sum() / G + rb.max()

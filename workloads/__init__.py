@@ -121,6 +121,30 @@ class Workload:
         rows = int((g + 1).sum()) + int(g[self.sampling].sum())
         return rows * self.V * es
 
+    def requests(self, lo: int, hi: int) -> "Workload":
+        """Requests [lo, hi) as a workload of their own (pure indexing: their target, draft,
+        token, uniform rows and temperatures; CSR offsets rebased to 0). Requests are
+        independent, so its results are the matching slice of the whole batch's."""
+        assert 0 <= lo < hi <= self.B
+        g = self.gammas
+        t0 = int(self.target_base[lo])
+        t1 = int(self.target_base[hi - 1] + g[hi - 1] + 1)
+        d0 = int(self.draft_base[lo])
+        d1 = int(self.draft_base[hi - 1] + g[hi - 1])
+        cu = None
+        if self.cu_draft is not None:
+            cu = (self.cu_draft[lo:hi + 1] - self.cu_draft[lo]).astype(self.cu_draft.dtype)
+        return Workload(f"{self.name} requests {lo}..{hi - 1}", self.dtype, hi - lo,
+                        self.gamma if cu is None else int(g[lo:hi].max()), self.V,
+                        self.target[t0:t1], self.draft[d0:d1], self.draft_tokens[d0:d1],
+                        self.uniforms[t0:t1], self.temperatures[lo:hi], cu, dict(self.meta))
+
+    def request_bytes(self) -> np.ndarray:
+        """Logit bytes each request needs read (its target rows, and its draft rows if it
+        samples): the per-request part of ``compulsory_bytes``."""
+        g = self.gammas
+        return ((g + 1) + np.where(self.sampling, g, 0)) * self.V * ELEM_SIZE[self.dtype]
+
     def as_greedy(self) -> "Workload":
         """Same tensors, every request at temperature 0."""
         return Workload(self.name + "-greedy", self.dtype, self.B, self.gamma, self.V,
@@ -248,6 +272,22 @@ CONFIG_NAMES = {
     4: "large-batch-sampling B=256 gamma=8 V=151936 f32 T=1.0 mixed-sigma",
     5: "ragged-mix B=512 gamma_b=U{1..8} V=128256 bf16 T=U[0,1.2] 20%-greedy",
 }
+
+
+def shard_ranges(w: Workload, G: int) -> list:
+    """Contiguous request ranges [lo, hi) for G GPUs, balanced by the logit bytes each request
+    needs (not by request count: requests of a ragged batch differ in rows): range k ends
+    at the first request where the running bytes reach (k + 1) / G of the total."""
+    assert 1 <= G <= w.B
+    c = np.cumsum(w.request_bytes())
+    ends = [int(np.searchsorted(c, c[-1] * (k + 1) / G, side="left")) + 1 for k in range(G)]
+    out, lo = [], 0
+    for k, e in enumerate(ends):
+        e = min(max(e, lo + 1), w.B - (G - 1 - k))  # every range non-empty
+        out.append((lo, e))
+        lo = e
+    assert out[-1][1] == w.B
+    return out
 
 
 def config(cid: int) -> Workload:
