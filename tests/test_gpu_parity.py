@@ -258,6 +258,33 @@ def test_random_calls_on_both_paths(i):
     np.testing.assert_array_equal(res[TWO]["num_accepted"][sure], res[ONE]["num_accepted"][sure])
 
 
+@PATHS
+def test_a_request_range_verifies_as_the_batch_slice(path):
+    # One GPU's share of a batch split by requests: the call over requests [lo, hi) alone
+    # matches the oracle, and on every request the oracle does not mark ambiguous it emits
+    # exactly what the whole batch's call emitted there (no state crosses requests; the
+    # row tiling may differ with the call's size, which only moves last-bit roundings)
+    temps = np.where(np.arange(24) % 4 == 0, 0.0, np.linspace(0.3, 1.2, 24))
+    w = workloads.small(B=24, gamma=6, V=20000, dtype="bf16", seed=314, ragged=True,
+                        temperatures=temps, draft_sigma=0.9)
+    o = oracle.verify(w)
+    full = run(w, path=path)
+    parity.compare(w, full, o)
+    for lo, hi in [(0, 7), (7, 8), (8, 24)]:
+        s = w.requests(lo, hi)
+        print(f"[gpu] requests {lo}..{hi - 1} of B={w.B} path={path}", flush=True)
+        g = run(s, path=path)
+        so = oracle.verify(s)
+        parity.compare(s, g, so)
+        sure = ~parity.ambiguous_requests(s, so)
+        t0 = int(w.target_base[lo])
+        for k in np.flatnonzero(sure):
+            tb, gb = int(s.target_base[k]), int(s.gammas[k])
+            np.testing.assert_array_equal(g["out_tokens"][tb: tb + gb + 1],
+                                          full["out_tokens"][t0 + tb: t0 + tb + gb + 1])
+        np.testing.assert_array_equal(g["num_accepted"][sure], full["num_accepted"][lo:hi][sure])
+
+
 # ----------------------------------------------------------------------- edge cases
 
 @PATHS
