@@ -424,10 +424,12 @@ def test_masked_logits(path, dtype):
 
 
 def test_requests_beyond_one_grid_dimension():
-    # 70000 requests: more row slots (210000) than one grid dimension holds, and more requests
-    # than the finishing launch's y dimension, so the z dimension carries the rest in both
-    w = workloads.small(B=70000, gamma=1, V=40, dtype="f32", seed=70, draft_sigma=0.8,
-                        temperatures=np.where(np.arange(70000) % 3 == 0, 0.0, 0.9))
+    # 528280 requests: more row slots (1584840) than one grid dimension holds, and more groups
+    # of eight requests (66035) than the finishing launch's y dimension, so the z dimension
+    # carries the rest in both launches
+    B = 8 * 65535 + 4000
+    w = workloads.small(B=B, gamma=1, V=16, dtype="f32", seed=70, draft_sigma=0.8,
+                        temperatures=np.where(np.arange(B) % 3 == 0, 0.0, 0.9))
     _both(w)
     _both(w, greedy=True)
 
