@@ -411,6 +411,40 @@ __device__ __forceinline__ double wave_sum(double v) {
   return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
+// A lane move that reaches every lane (quad permutations, row rotations): no value to set up
+// for lanes that receive nothing.
+template <int CTRL>
+__device__ __forceinline__ double dpp_all(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(unsigned)b, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(unsigned)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) |
+                                          (unsigned long long)(unsigned)lo));
+}
+// Four sums over the wavefront at once (every lane active): v[q] is lane l's term of sum q.
+// Two exchange steps transpose them, each lane keeping half of its terms and receiving its
+// partner's half of the others (quad partners l ^ 1, then l ^ 2), so lane l then holds one
+// sum, q(l) = 2 (l & 1) + ((l >> 1) & 1), over its quad; row rotations by 4 and 8 and the
+// exchanges with lanes l ^ 16 and l ^ 32 complete it over the wavefront.  Every lane returns
+// the total of sum q(l) (lanes 0..3 hold sums 0, 2, 1, 3).  About a third of the lane moves
+// and adds of four wave_sum calls, in a chain of the same depth.
+__device__ __forceinline__ double wave_sum4(const double (&v)[4], int lane) {
+  const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
+  // step 1: keep sums {2 b0, 2 b0 + 1}, send the other two
+  const double s0 = b0 ? v[0] : v[2], s1 = b0 ? v[1] : v[3];
+  const double k0 = b0 ? v[2] : v[0], k1 = b0 ? v[3] : v[1];
+  const double e0 = k0 + dpp_all<0xB1>(s0);  // quad_perm [1, 0, 3, 2]
+  const double e1 = k1 + dpp_all<0xB1>(s1);
+  // step 2: keep sum 2 b0 + b1
+  const double s = b1 ? e0 : e1, k = b1 ? e1 : e0;
+  double f = k + dpp_all<0x4E>(s);  // quad_perm [2, 3, 0, 1]
+  f += dpp_all<0x124>(f);           // row_ror:4
+  f += dpp_all<0x128>(f);           // row_ror:8
+  f += __shfl_xor(f, 16);
+  f += __shfl_xor(f, 32);
+  return f;
+}
+
 // The same reduction pattern for 32-bit values; rows that do not receive a move get `id`,
 // the operation's identity.
 template <int CTRL, int ROWS>
@@ -1121,20 +1155,47 @@ __device__ __forceinline__ void stream_chunks(const Params &P, const Stop &st, i
       rt[q] = u < ub_end ? U::template load<false>(tr, u) : U::filler();
       rd[q] = resid && u < ub_end ? U::template load<false>(dr, u) : U::filler();
     }
+    if constexpr (RU == 4) {
+      // the pass's four chunks reduced together; lane q(l) < 4 stores chunk q(l)'s sum
+      double d[4];
 #pragma unroll
-    for (int q = 0; q < RU; ++q) {
-      const int64_t c0 = ub + q * NT + wave * 64;  // first unit of this chunk
-      if (c0 >= ub_end) break;  // uniform across the wavefront
-      float zt[W], zd[W], r[W];
-      U::cvt(rt[q], zt);
-      U::cvt(rd[q], zd);
-      if constexpr (ACC)
-        resid_weights_acc<W>(zt, zd, st, kd, r);
-      else
-        resid_weights<W>(zt, zd, st, r);
-      const float us = unit_sum<W>(r);
-      const double sum = wave_sum(c0 + lane < ub_end ? (double)us : 0.0);
-      if (lane == 0) share_store(&cs[c0 / kChunkUnits], sum);
+      for (int q = 0; q < 4; ++q) {
+        const int64_t c0 = ub + q * NT + wave * 64;  // first unit of this chunk
+        d[q] = 0.0;
+        if (c0 < ub_end) {  // uniform across the wavefront
+          float zt[W], zd[W], r[W];
+          U::cvt(rt[q], zt);
+          U::cvt(rd[q], zd);
+          if constexpr (ACC)
+            resid_weights_acc<W>(zt, zd, st, kd, r);
+          else
+            resid_weights<W>(zt, zd, st, r);
+          const float us = unit_sum<W>(r);
+          d[q] = c0 + lane < ub_end ? (double)us : 0.0;
+        }
+      }
+      const double sum = wave_sum4(d, lane);
+      if (lane < 4) {
+        const int q = 2 * (lane & 1) + ((lane >> 1) & 1);
+        const int64_t c0 = ub + q * NT + wave * 64;
+        if (c0 < ub_end) share_store(&cs[c0 / kChunkUnits], sum);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < RU; ++q) {
+        const int64_t c0 = ub + q * NT + wave * 64;  // first unit of this chunk
+        if (c0 >= ub_end) break;  // uniform across the wavefront
+        float zt[W], zd[W], r[W];
+        U::cvt(rt[q], zt);
+        U::cvt(rd[q], zd);
+        if constexpr (ACC)
+          resid_weights_acc<W>(zt, zd, st, kd, r);
+        else
+          resid_weights<W>(zt, zd, st, r);
+        const float us = unit_sum<W>(r);
+        const double sum = wave_sum(c0 + lane < ub_end ? (double)us : 0.0);
+        if (lane == 0) share_store(&cs[c0 / kChunkUnits], sum);
+      }
     }
   }
 }
