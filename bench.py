@@ -376,6 +376,19 @@ def read_floors(m: Measured) -> dict:
             "reads_only_frac": round(m.nbytes / (floor * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
+def finish_figures(m: Measured, floors: dict):
+    """The finishing kernel against its own bytes: the stop rows it re-reads (overhead of the
+    method, not in the metric's denominator) over its mean duration, beside the plain read
+    stream's time for the same bytes.  None on the one-launch path."""
+    us = m.per_kernel_us.get("k_finish")
+    if us is None or not m.stop_bytes:
+        return None
+    gbps = m.stop_bytes / (us * 1e-6) / 1e9
+    return {"kernel": "k_finish", "kernel_us": round(us, 2), "stop_row_bytes": m.stop_bytes,
+            "GB_per_s": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "read_stop_row_bytes_us": floors["read_stop_row_bytes_us"]}
+
+
 def rnd(x):
     return None if x is None else round(x, 2)
 
@@ -394,6 +407,7 @@ def config_entry(m: Measured) -> dict:
     line; the 70%-of-peak bar is stated per call)."""
     w = m.w
     frac = m.logit_gbps / HBM_PEAK_GBPS
+    floors = read_floors(m)
     return {"workload": f"{m.workload_id}: {w.name}", "B": w.B, "gamma_max": w.gamma, "V": w.V,
             "logit_dtype": w.dtype, "logit_bytes_per_step": m.nbytes,
             "entry_point": "spec_verify_greedy" if m.all_greedy else "spec_verify_sample",
@@ -411,7 +425,8 @@ def config_entry(m: Measured) -> dict:
                 traffic_for_current_kernel(m.kernels[0], m.workload_id)),
             "step_kernel_us_p10_p50_p90": [round(float(np.percentile(m.step_kernels, q)), 1)
                                            for q in (10, 50, 90)],
-            "read_reference": read_floors(m)}
+            "read_reference": floors,
+            "finish": finish_figures(m, floors)}
 
 
 def main():
@@ -526,8 +541,9 @@ def main():
                      "frac": round(m.achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else traffic["hbm_bytes_per_launch"]},
         "cpu_baseline": None,
-        "read_reference": read_floors(m),
     }
+    result["read_reference"] = read_floors(m)
+    result["finish"] = finish_figures(m, result["read_reference"])
     result["commit"] = time_commit(sv, w, m.out, m.nacc, d=m.inputs[0], steps=args.steps)
     if args.streams > 1:
         result["independent_batches"] = time_streams(sv, w, m.inputs, m.code, path,
